@@ -1,0 +1,205 @@
+// extern "C" entry points of libfp4q: argument validation on the host, then
+// dispatch to the HIP launchers.  Validation touches no HIP API, so every
+// argument error is reported before anything is enqueued (and on machines
+// without a GPU).
+#include "../../include/fp4q.h"
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "fp4q_internal.hpp"
+
+namespace {
+
+using namespace fp4q;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_format(int f) { return f >= FP4Q_NVFP4 && f <= FP4Q_NVFP4_RAZER_W; }
+
+// RaZeR special value: multiple of 0.5 (RaZeR summary 2.2), 0 < |v| <= 7.5 so
+// that value * scale stays exact in the matmul's f16 decode, and not one of
+// the standard E2M1 magnitudes
+bool valid_special(float v) {
+  if (!std::isfinite(v)) return false;
+  float a = std::fabs(v);
+  if (!(a > 0.0f && a <= 7.5f)) return false;
+  float twice = a * 2.0f;
+  if (twice != std::floor(twice)) return false;
+  static const float kStd[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  for (float s : kStd)
+    if (a == s) return false;
+  return true;
+}
+
+fp4q_status check_desc(const fp4q_quant_desc* d, bool quantizing) {
+  if (!d) return FP4Q_ERR_NULL;
+  if (d->struct_size != sizeof(fp4q_quant_desc)) return FP4Q_ERR_ARG;
+  if (!valid_format(d->format)) return FP4Q_ERR_FORMAT;
+  if (d->format == FP4Q_MXFP4) {
+    if (d->block != 32) return FP4Q_ERR_ARG;
+  } else if (d->block != 4 && d->block != 8 && d->block != 16 && d->block != 32) {
+    return FP4Q_ERR_ARG;
+  }
+  if (d->format == FP4Q_NVFP4_RAZER_W)
+    for (int i = 0; i < 4; ++i)
+      if (!valid_special(d->special[i])) return FP4Q_ERR_ARG;
+  if (!quantizing) return FP4Q_OK;
+  const uint32_t rule = d->rule & 0xFFu, flags = d->rule & ~0xFFu;
+  if (flags & ~(uint32_t)FP4Q_FLAG_PREVENT_ZERO) return FP4Q_ERR_ARG;
+  if (rule > FP4Q_RULE_BRUTE) return FP4Q_ERR_ARG;
+  if (d->format != FP4Q_NVFP4 && rule != FP4Q_RULE_ABSMAX) return FP4Q_ERR_ARG;
+  if (d->format == FP4Q_MXFP4 && flags) return FP4Q_ERR_ARG;
+  if (d->global_mode < FP4Q_GLOBAL_NONE || d->global_mode > FP4Q_GLOBAL_GIVEN) return FP4Q_ERR_ARG;
+  if (d->format == FP4Q_MXFP4 && d->global_mode != FP4Q_GLOBAL_NONE) return FP4Q_ERR_ARG;
+  if (d->hadamard != 0 && d->hadamard != 32) return FP4Q_ERR_ARG;
+  return FP4Q_OK;
+}
+
+fp4q_status device_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_DEVICE; }
+
+size_t elem_size(fp4q_dtype t) { return t == FP4Q_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+fp4q_status fp4q_quantize(const fp4q_quant_desc* desc, const void* x, fp4q_dtype x_dtype,
+                          int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                          uint8_t* scales, float* global, void* stream) {
+  fp4q_status st = check_desc(desc, true);
+  if (st != FP4Q_OK) return st;
+  if (x_dtype != FP4Q_F32 && x_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!x || !codes || !scales) return FP4Q_ERR_NULL;
+  if (desc->global_mode != FP4Q_GLOBAL_NONE && !global) return FP4Q_ERR_NULL;
+  if (rows < 0 || cols <= 0 || ld_x < cols || cols % desc->block != 0) return FP4Q_ERR_SHAPE;
+  if (desc->hadamard == 32 && cols % 32 != 0) return FP4Q_ERR_SHAPE;
+  if (!aligned16(x) || (ld_x * (int64_t)elem_size(x_dtype)) % 16 != 0 || !aligned16(codes))
+    return FP4Q_ERR_ALIGN;
+  if (desc->chan_scale && !aligned16(desc->chan_scale)) return FP4Q_ERR_ALIGN;
+  if (global && ((uintptr_t)global & 3u)) return FP4Q_ERR_ALIGN;
+
+  QuantParams p{};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld_x;
+  p.x_bf16 = x_dtype == FP4Q_BF16;
+  p.codes = codes;
+  p.scales = scales;
+  p.global = desc->global_mode == FP4Q_GLOBAL_NONE ? nullptr : global;
+  p.chan_scale = desc->chan_scale;
+  p.hadamard = desc->hadamard;
+  p.prevent_zero = (desc->rule & FP4Q_FLAG_PREVENT_ZERO) != 0;
+  for (int i = 0; i < 4; ++i) p.special[i] = desc->special[i];
+  return device_status(launch_quantize(desc->format, desc->block, (int)(desc->rule & 0xFFu),
+                                       desc->global_mode, p, (hipStream_t)stream));
+}
+
+fp4q_status fp4q_dequantize(const fp4q_quant_desc* desc, const uint8_t* codes,
+                            const uint8_t* scales, const float* global, int64_t rows,
+                            int64_t cols, void* out, fp4q_dtype out_dtype, int64_t ld_out,
+                            void* stream) {
+  fp4q_status st = check_desc(desc, false);
+  if (st != FP4Q_OK) return st;
+  if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!codes || !scales || !out) return FP4Q_ERR_NULL;
+  if (rows < 0 || cols <= 0 || ld_out < cols || cols % desc->block != 0) return FP4Q_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(out) || (ld_out * (int64_t)elem_size(out_dtype)) % 16 != 0)
+    return FP4Q_ERR_ALIGN;
+  if (global && ((uintptr_t)global & 3u)) return FP4Q_ERR_ALIGN;
+  DequantParams p{};
+  p.codes = codes;
+  p.scales = scales;
+  p.global = global;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_out = ld_out;
+  p.out = out;
+  p.out_bf16 = out_dtype == FP4Q_BF16;
+  for (int i = 0; i < 4; ++i) p.special[i] = desc->special[i];
+  return device_status(launch_dequantize(desc->format, desc->block, p, (hipStream_t)stream));
+}
+
+fp4q_status fp4q_gemm_w4a4(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const float* a_global, fp4q_format fw, const uint8_t* w_codes,
+                           const uint8_t* w_scales, const float* w_global,
+                           const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
+                           fp4q_dtype c_dtype, int64_t ldc, void* stream) {
+  if (!valid_format(fa) || !valid_format(fw)) return FP4Q_ERR_FORMAT;
+  if ((fa == FP4Q_MXFP4) != (fw == FP4Q_MXFP4) || fa == FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
+  if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
+  if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
+  const int64_t block = fa == FP4Q_MXFP4 ? 32 : 16;
+  if (M < 0 || N < 0 || K <= 0 || K % block != 0 || ldc < N) return FP4Q_ERR_SHAPE;
+  if (fw == FP4Q_NVFP4_RAZER_W)
+    for (int i = 0; i < 4; ++i)
+      if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(c) ||
+      (ldc * (int64_t)elem_size(c_dtype)) % 16 != 0)
+    return FP4Q_ERR_ALIGN;
+  if ((a_global && ((uintptr_t)a_global & 3u)) || (w_global && ((uintptr_t)w_global & 3u)))
+    return FP4Q_ERR_ALIGN;
+  GemmParams p{};
+  p.a_codes = a_codes;
+  p.a_scales = a_scales;
+  p.a_global = a_global;
+  p.w_codes = w_codes;
+  p.w_scales = w_scales;
+  p.w_global = w_global;
+  for (int i = 0; i < 4; ++i) p.w_special[i] = (fw == FP4Q_NVFP4_RAZER_W) ? w_special[i] : 0.0f;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  p.c_bf16 = c_dtype == FP4Q_BF16;
+  return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream));
+}
+
+fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x, int64_t ldx,
+                               const void* w, fp4q_dtype w_dtype, int64_t rows_w, int64_t ldw,
+                               int64_t cols, double alpha, float* t, float* r, void* stream) {
+  if ((x_dtype != FP4Q_F32 && x_dtype != FP4Q_BF16) || (w_dtype != FP4Q_F32 && w_dtype != FP4Q_BF16))
+    return FP4Q_ERR_ARG;
+  if (!x || !w || !t || !r) return FP4Q_ERR_NULL;
+  if (rows_x <= 0 || rows_w <= 0 || cols <= 0 || ldx < cols || ldw < cols) return FP4Q_ERR_SHAPE;
+  if (!std::isfinite(alpha)) return FP4Q_ERR_ARG;
+  if (((uintptr_t)x % elem_size(x_dtype)) || ((uintptr_t)w % elem_size(w_dtype)) ||
+      ((uintptr_t)t & 3u) || ((uintptr_t)r & 3u))
+    return FP4Q_ERR_ALIGN;
+  ChanScaleParams p{};
+  p.x = x;
+  p.x_bf16 = x_dtype == FP4Q_BF16;
+  p.rows_x = rows_x;
+  p.ldx = ldx;
+  p.w = w;
+  p.w_bf16 = w_dtype == FP4Q_BF16;
+  p.rows_w = rows_w;
+  p.ldw = ldw;
+  p.cols = cols;
+  p.alpha = alpha;
+  p.t = t;
+  p.r = r;
+  return device_status(launch_channel_scale(p, (hipStream_t)stream));
+}
+
+const char* fp4q_status_string(fp4q_status s) {
+  switch (s) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_ERR_NULL: return "a required pointer is NULL";
+    case FP4Q_ERR_SHAPE: return "sizes are negative or not divisible as required";
+    case FP4Q_ERR_ALIGN: return "a pointer or row pitch is not 16-byte aligned";
+    case FP4Q_ERR_FORMAT: return "unknown format or unsupported format pair";
+    case FP4Q_ERR_ARG: return "bad rule, mode, block, transform or special value";
+    case FP4Q_ERR_UNSUPPORTED: return "combination not implemented";
+    case FP4Q_ERR_DEVICE: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+uint32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+}  // extern "C"

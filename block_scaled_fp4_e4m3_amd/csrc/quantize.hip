@@ -1,0 +1,665 @@
+// Block-scaled FP4 quantization, dequantization, global amax and channel
+// scale kernels for gfx950.
+//
+// Pages: scale rules -- "Finer is Better (with the Right Scaling)", Method 2
+// (abs-max, prevent-zero, 4-over-6, brute-force, hierarchical); RaZeR picks --
+// RaZeR summary, sections 2.1 and 2.2; MXFP4 and the online transforms --
+// MACaQ review, sections 1 and 3.
+//
+// Exactness.  Every rounding decision is the exact real-arithmetic one.  A
+// decision "is |x| past T" with T = m * s * g (m a midpoint of at most 5
+// significant bits, s a scale of at most 4, g an FP32) is reduced to one
+// unsigned compare of FP32 bit patterns: |x| > T  <=>  |x| > RD32(T), and
+// |x| >= T  <=>  |x| >= RU32(T).  T is formed exactly in binary64 and rounded
+// down or up to FP32 once per workgroup, into LDS tables indexed by the scale
+// code.  A tie goes to the even neighbour, so each threshold is stored as the
+// strict-greater form of either RD (tie stays low) or RU (tie goes up).
+//
+// Work mapping.  One lane owns L = 8 consecutive elements of a row (L = 4 for
+// blocks of 4): one 128-bit load of bf16 (two of fp32).  A block of B >= L
+// elements spans B/L adjacent lanes; block maxima and error sums cross lanes
+// with xor shuffles, which reproduces the balanced pairwise error tree
+// (each lane sums its L elements as a balanced tree first).
+#include "fp4q_internal.hpp"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+// strict-greater threshold bits for "round up past T" decisions:
+// tie_up = false:  |x| > T  <=>  bits(|x|) > bits(RD32(T))
+// tie_up = true :  |x| >= T <=>  bits(|x|) > bits(RU32(T)) - 1
+__device__ __forceinline__ uint32_t thr_bits(double T, bool tie_up) {
+  float f = (float)T;  // nearest
+  uint32_t b = fbits(f);
+  if (!tie_up) {
+    if ((double)f > T) b -= 1;  // RD
+    return b;
+  }
+  if ((double)f < T) b += 1;    // RU
+  return b - 1;
+}
+// |x| < T  <=>  bits(|x|) < bits(RU32(T))
+__device__ __forceinline__ uint32_t ru_bits(double T) {
+  float f = (float)T;
+  uint32_t b = fbits(f);
+  if ((double)f < T) b += 1;
+  return b;
+}
+
+// scale-format values (binary64, exact)
+template <int SF>  // 0: E4M3 (codes 0..126), 1: E3M3 (codes 0..63)
+__device__ __forceinline__ double sf_val(int k) {
+  int e = k >> 3, m = k & 7;
+  if (SF == 0) return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return e == 0 ? ldexp((double)m, -5) : ldexp((double)(8 + m), e - 6);
+}
+
+// E2M1 magnitudes and the midpoints between neighbours
+__constant__ float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+__constant__ float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+
+template <int FMT> struct FmtTraits;
+template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
+template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0, KMAX = 126, NSP = 2; };
+template <> struct FmtTraits<RAZER_W> { static constexpr int SF = 1, KMAX = 63,  NSP = 4; };
+template <> struct FmtTraits<MXFP4>   { static constexpr int SF = 2, KMAX = 0,   NSP = 0; };
+
+// LDS tables, built once per workgroup for the launch's global scale g
+template <int FMT>
+struct Tables {
+  static constexpr int KN = FmtTraits<FMT>::KMAX + 1;
+  static constexpr int NSP = FmtTraits<FMT>::NSP > 0 ? FmtTraits<FMT>::NSP : 1;
+  uint32_t elt[KN][8];        // per scale code: 7 element thresholds (strict >)
+  uint32_t smid6[KN];         // scale midpoints for T = 6 (strict >), last unused
+  uint32_t smid4[KN];         // scale midpoints for T = 4
+  uint32_t sp_lo[KN][NSP];    // special interval, strict >
+  uint32_t sp_hi[KN][NSP];    // special interval, strict <
+  float spv[NSP];             // special values
+};
+template <> struct Tables<MXFP4> { uint32_t dummy; };
+
+// Nearest standard E2M1 magnitudes below/above |v| (|v| in (2, 7.5], not on the grid)
+__device__ __forceinline__ void special_bounds(float av, float& lo, float& hi, bool& open_hi) {
+  float below = 0.f, above = 0.f;
+  open_hi = true;
+  for (int m = 0; m < 8; ++m) {
+    if (kMag[m] < av) below = kMag[m];
+    if (kMag[m] > av && open_hi) { above = kMag[m]; open_hi = false; }
+  }
+  lo = 0.5f * (below + av);
+  hi = 0.5f * (above + av);
+}
+
+template <int FMT>
+__device__ void build_tables(Tables<FMT>& T, float g, const float* special) {
+  if constexpr (FMT != MXFP4) {
+    constexpr int SF = FmtTraits<FMT>::SF;
+    constexpr int KN = Tables<FMT>::KN;
+    constexpr int NSP = FmtTraits<FMT>::NSP;
+    const double gd = (double)g;
+    for (int i = threadIdx.x; i < KN * 8; i += blockDim.x) {
+      int k = i >> 3, j = i & 7;
+      uint32_t v = 0x7F800000u;  // never passed by a finite |x|
+      if (k > 0 && j < 7) v = thr_bits((double)kMid[j] * sf_val<SF>(k) * gd, (j & 1) != 0);
+      T.elt[k][j] = v;
+    }
+    for (int i = threadIdx.x; i < 2 * KN; i += blockDim.x) {
+      int k = i % KN, which = i / KN;
+      uint32_t v = 0xFFFFFFFFu;
+      if (k < KN - 1) {
+        double mid = 0.5 * (sf_val<SF>(k) + sf_val<SF>(k + 1));
+        v = thr_bits(mid * (which ? 4.0 : 6.0) * gd, (k & 1) != 0);  // tie -> even code
+      }
+      if (which) T.smid4[k] = v; else T.smid6[k] = v;
+    }
+    if constexpr (NSP > 0) {
+      for (int i = threadIdx.x; i < KN * NSP; i += blockDim.x) {
+        int k = i / NSP, p = i % NSP;
+        float v = (FMT == RAZER_A) ? (p == 0 ? 5.0f : -5.0f) : special[p];
+        float lo, hi; bool open_hi;
+        special_bounds(fabsf(v), lo, hi, open_hi);
+        double s = sf_val<SF>(k) * gd;
+        T.sp_lo[k][p] = (k == 0) ? 0x7F800000u : thr_bits((double)lo * s, false);
+        T.sp_hi[k][p] = (k == 0 || open_hi) ? 0x7F800000u : ru_bits((double)hi * s);
+        if (k == 0) T.spv[p] = v;
+      }
+    }
+  }
+}
+
+// nearest scale code to a/(T g) from the midpoint table; guess in binary64
+template <int SF>
+__device__ __forceinline__ int select_scale(float a, const uint32_t* smid, double inv_Tg) {
+  constexpr int KMAX = SF == 0 ? 126 : 63;
+  double y = (double)a * inv_Tg;
+  int k;
+  if (SF == 0) {
+    if (!(y < 448.0)) k = KMAX;
+    else if (y < 0.015625) k = (int)(y * 512.0);
+    else {
+      uint64_t b = (uint64_t)__double_as_longlong(y);
+      int e = (int)((b >> 52) & 0x7FF) - 1023;
+      k = ((e + 7) << 3) | (int)((b >> 49) & 7);
+    }
+  } else {
+    if (!(y < 30.0)) k = KMAX;
+    else if (y < 0.25) k = (int)(y * 32.0);
+    else {
+      uint64_t b = (uint64_t)__double_as_longlong(y);
+      int e = (int)((b >> 52) & 0x7FF) - 1023;
+      k = ((e + 3) << 3) | (int)((b >> 49) & 7);
+    }
+  }
+  uint32_t ab = fbits(a);
+  if (k < KMAX && ab > smid[k]) ++k;
+  else if (k > 0 && ab <= smid[k - 1]) --k;
+  return k;
+}
+
+// E2M1 magnitude index of |x| (bits xb) against 7 non-decreasing thresholds
+__device__ __forceinline__ int rtn_mag(uint32_t xb, const uint32_t t[7]) {
+  bool c2 = xb > t[3];
+  uint32_t s1 = c2 ? t[5] : t[1];
+  bool c1 = xb > s1;
+  uint32_t s0 = c2 ? (c1 ? t[6] : t[4]) : (c1 ? t[2] : t[0]);
+  bool c0 = xb > s0;
+  return (c2 ? 4 : 0) | (c1 ? 2 : 0) | (c0 ? 1 : 0);
+}
+
+template <int L>
+struct Chunk {
+  float x[L];
+};
+
+template <int L>
+__device__ __forceinline__ float tree_sum(const float* p) {
+  if constexpr (L == 4) return (p[0] + p[1]) + (p[2] + p[3]);
+  else return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// load L elements of row r starting at column j0, apply the channel scale and
+// the size-32 block-Hadamard (lanes of a 32-group are adjacent)
+template <int L, bool BF16>
+__device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int64_t j0, float* x,
+                                           bool chan, bool had) {
+  if constexpr (BF16) {
+    const uint16_t* src = (const uint16_t*)p.x + r * p.ld + j0;
+    if constexpr (L == 8) {
+      uint4 v = *(const uint4*)src;
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
+    } else {
+      uint2 v = *(const uint2*)src;
+      uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
+    }
+  } else {
+    const float* src = (const float*)p.x + r * p.ld + j0;
+#pragma unroll
+    for (int i = 0; i < L; i += 4) {
+      float4 v = *(const float4*)(src + i);
+      x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+    }
+  }
+  if (chan) {
+#pragma unroll
+    for (int i = 0; i < L; i += 4) {
+      float4 t = *(const float4*)(p.chan_scale + j0 + i);
+      x[i] = x[i] * t.x; x[i + 1] = x[i + 1] * t.y; x[i + 2] = x[i + 2] * t.z; x[i + 3] = x[i + 3] * t.w;
+    }
+  }
+  if (had) {
+    // in-lane stages h < L
+#pragma unroll
+    for (int h = 1; h < L; h *= 2) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        if ((i & h) == 0) {
+          float u = x[i], w = x[i + h];
+          x[i] = u + w;
+          x[i + h] = u - w;
+        }
+      }
+    }
+    // cross-lane stages h = L .. 16 with partner lane ^ (h / L)
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 32 / L; d *= 2) {
+      const bool lower = (lane & d) == 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        float o = __shfl_xor(x[i], d);
+        x[i] = lower ? (x[i] + o) : (o - x[i]);
+      }
+    }
+    const float c = bitsf(0x3E3504F3u);  // RN32(2^-2.5)
+#pragma unroll
+    for (int i = 0; i < L; ++i) x[i] = x[i] * c;
+  }
+}
+
+// encode L elements with thresholds t; returns packed nibbles
+template <int L>
+__device__ __forceinline__ uint32_t encode_plain(const float* x, const uint32_t t[7]) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    uint32_t b = fbits(x[i]);
+    int m = rtn_mag(b & 0x7FFFFFFFu, t);
+    uint32_t c = m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u;
+    packed |= c << (4 * i);
+  }
+  return packed;
+}
+
+// RaZeR: standard code unless |x| lies strictly inside the special interval
+// with the special value's sign, then 0x8
+template <int L>
+__device__ __forceinline__ uint32_t encode_special(const float* x, const uint32_t t[7], uint32_t lo,
+                                                   uint32_t hi, uint32_t vsign) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    uint32_t b = fbits(x[i]);
+    uint32_t xb = b & 0x7FFFFFFFu;
+    int m = rtn_mag(xb, t);
+    uint32_t c = m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u;
+    bool sp = ((b & 0x80000000u) == vsign) && xb > lo && xb < hi;
+    packed |= (sp ? 8u : c) << (4 * i);
+  }
+  return packed;
+}
+
+// block error of a lane's L elements (lane part of the balanced tree);
+// value of a code via the hardware FP4 -> FP32 convert (scale 1.0 is exact)
+template <int L>
+__device__ __forceinline__ float lane_sse(const float* x, uint32_t packed, float s, float g,
+                                          bool has_sp, float vs) {
+  float p[L];
+  static_for<0, L / 2>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;  // byte b holds elements 2b, 2b+1
+    auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, b);
+    float q0 = v2[0] * s, q1 = v2[1] * s;
+    if (has_sp) {
+      if (((packed >> (8 * b)) & 15u) == 8u) q0 = vs;
+      if (((packed >> (8 * b + 4)) & 15u) == 8u) q1 = vs;
+    }
+    float e0 = __builtin_fmaf(-q0, g, x[2 * b]);
+    float e1 = __builtin_fmaf(-q1, g, x[2 * b + 1]);
+    p[2 * b] = e0 * e0;
+    p[2 * b + 1] = e1 * e1;
+  });
+  return tree_sum<L>(p);
+}
+
+template <int LPB>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int d = 1; d < LPB; d *= 2) v = v + __shfl_xor(v, d);
+  return v;
+}
+template <int LPB>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < LPB; d *= 2) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+  return v;
+}
+
+template <int FMT, int B, int RULE, bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
+  constexpr int L = (B == 4) ? 4 : 8;
+  constexpr int LPB = B / L;  // lanes per block
+  __shared__ Tables<FMT> T;
+  const float g = p.global ? *p.global : 1.0f;
+  build_tables<FMT>(T, g, p.special);
+  __syncthreads();
+
+  const bool chan = p.chan_scale != nullptr;
+  const bool had = p.hadamard == 32;
+  const int64_t cpr = p.cols / L;            // chunks per row
+  const int64_t total = p.rows * cpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const double inv6 = 1.0 / (6.0 * (double)g);
+  const double inv4 = 1.0 / (4.0 * (double)g);
+  constexpr int SF = FmtTraits<FMT>::SF;
+
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c - threadIdx.x < total; c += stride) {
+    // whole waves stay in the loop so that shuffles see their partners; lanes
+    // past the end work on a clamped chunk and store nothing
+    const bool valid = c < total;
+    const int64_t cc = valid ? c : total - 1;
+    const int64_t r = cc / cpr, cj = cc % cpr;
+    float x[L];
+    load_chunk<L, BF16>(p, r, cj * L, x, chan, had);
+
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+    amax = group_max<LPB>(amax);
+
+    uint32_t packed;
+    uint8_t sbyte;
+    if constexpr (FMT == MXFP4) {
+      // MACaQ section 1: shared exponent E = floor(log2 amax) - 2, clamped
+      int E;
+      if (amax == 0) E = -127;
+      else {
+        int ex = (int)(amax >> 23);
+        int fl = ex ? ex - 127 : (31 - __clz((int)amax)) - 149;
+        E = max(-127, fl - 2);
+      }
+      uint32_t t[7];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        uint32_t b = fbits(ldexpf(kMid[j], E));   // exact
+        t[j] = (j & 1) ? b - 1 : b;
+      }
+      packed = encode_plain<L>(x, t);
+      sbyte = (uint8_t)(E + 127);
+    } else if constexpr (FMT == NVFP4) {
+      if constexpr (RULE == BRUTE) {
+        // every positive E4M3 scale; strict minimum, ties keep the smaller code
+        float best = 0.f;
+        int bestk = 1;
+        packed = 0;
+        for (int k = 1; k <= 126; ++k) {
+          uint32_t t[7];
+#pragma unroll
+          for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
+          uint32_t pk = encode_plain<L>(x, t);
+          float e = group_sum<LPB>(lane_sse<L>(x, pk, (float)sf_val<0>(k), g, false, 0.f));
+          if (k == 1 || e < best) { best = e; bestk = k; packed = pk; }
+        }
+        sbyte = (uint8_t)bestk;
+      } else {
+        int k6 = select_scale<0>(bitsf(amax), T.smid6, inv6);
+        if (p.prevent_zero && k6 == 0) k6 = 1;
+        uint32_t t[7];
+#pragma unroll
+        for (int j = 0; j < 7; ++j) t[j] = T.elt[k6][j];
+        packed = encode_plain<L>(x, t);
+        sbyte = (uint8_t)k6;
+        if constexpr (RULE == FOUR6) {
+          int k4 = select_scale<0>(bitsf(amax), T.smid4, inv4);
+          if (p.prevent_zero && k4 == 0) k4 = 1;
+#pragma unroll
+          for (int j = 0; j < 7; ++j) t[j] = T.elt[k4][j];
+          uint32_t pk4 = encode_plain<L>(x, t);
+          float e6 = group_sum<LPB>(lane_sse<L>(x, packed, (float)sf_val<0>(k6), g, false, 0.f));
+          float e4 = group_sum<LPB>(lane_sse<L>(x, pk4, (float)sf_val<0>(k4), g, false, 0.f));
+          if (e4 < e6) { packed = pk4; sbyte = (uint8_t)k4; }
+        }
+      }
+    } else {
+      // RaZeR: abs-max scale (E4M3 for activations, E3M3 for weights), then
+      // the special value with the lowest block error (ties keep the first)
+      int k = select_scale<SF>(bitsf(amax), T.smid6, inv6);
+      if (p.prevent_zero && k == 0) k = 1;
+      uint32_t t[7];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
+      const float s = (float)sf_val<SF>(k);
+      constexpr int NSP = FmtTraits<FMT>::NSP;
+      float best = 0.f;
+      int bestp = 0;
+      packed = 0;
+      if (k == 0) {
+        packed = 0;
+      } else {
+#pragma unroll
+        for (int q = 0; q < NSP; ++q) {
+          float v = T.spv[q];
+          uint32_t pk = encode_special<L>(x, t, T.sp_lo[k][q], T.sp_hi[k][q], fbits(v) & 0x80000000u);
+          float e = group_sum<LPB>(lane_sse<L>(x, pk, s, g, true, v * s));
+          if (q == 0 || e < best) { best = e; bestp = q; packed = pk; }
+        }
+      }
+      if (FMT == RAZER_A) sbyte = (uint8_t)((bestp << 7) | k);
+      else sbyte = (uint8_t)((bestp << 6) | k);
+    }
+
+    if (valid) {
+      uint8_t* dst = p.codes + r * (p.cols / 2) + cj * (L / 2);
+      if constexpr (L == 8) *(uint32_t*)dst = packed;
+      else *(uint16_t*)dst = (uint16_t)packed;
+      if (cj % LPB == 0) p.scales[r * (p.cols / B) + cj / LPB] = sbyte;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- global amax
+__global__ void zero_global_kernel(float* g) { *(uint32_t*)g = 0u; }
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(QuantParams p) {
+  constexpr int L = 8;
+  const bool chan = p.chan_scale != nullptr;
+  const bool had = p.hadamard == 32;
+  const int64_t cpr = p.cols / L;
+  const int64_t total = p.rows * cpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c - threadIdx.x < total; c += stride) {
+    const bool valid = c < total;
+    const int64_t cc = valid ? c : total - 1;
+    float x[L];
+    load_chunk<L, BF16>(p, cc / cpr, (cc % cpr) * L, x, chan, had);
+    if (valid)
+#pragma unroll
+      for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.global, m);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax4_kernel(QuantParams p) {
+  // columns that are a multiple of 4 but not 8 (blocks of 4 without Hadamard)
+  constexpr int L = 4;
+  const bool chan = p.chan_scale != nullptr;
+  const int64_t cpr = p.cols / L;
+  const int64_t total = p.rows * cpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total; c += stride) {
+    float x[L];
+    load_chunk<L, BF16>(p, c / cpr, (c % cpr) * L, x, chan, false);
+#pragma unroll
+    for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.global, m);
+}
+
+// "Finer is Better" Method 2 hierarchical scaling: g maps the tensor maximum
+// to the top of the two-level range: amax / (6*448) for E4M3 block scales,
+// amax / (6*30) for E3M3; 1 for an all-zero tensor
+__global__ void finalize_global_kernel(float* g, float denom) {
+  float a = bitsf(*(const uint32_t*)g);
+  *g = (a == 0.0f) ? 1.0f : a / denom;
+}
+
+// ---------------------------------------------------------------- dequantize
+template <int FMT, int B>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantParams p) {
+  constexpr int L = (B == 4) ? 4 : 8;
+  const float g = p.global ? *p.global : 1.0f;
+  const int64_t cpr = p.cols / L;
+  const int64_t total = p.rows * cpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total; c += stride) {
+    const int64_t r = c / cpr, cj = c % cpr, j0 = cj * L;
+    const uint8_t* src = p.codes + r * (p.cols / 2) + j0 / 2;
+    uint32_t packed = (L == 8) ? *(const uint32_t*)src : (uint32_t)*(const uint16_t*)src;
+    const uint8_t sb = p.scales[r * (p.cols / B) + j0 / B];
+    float s, v = 0.f;
+    if constexpr (FMT == MXFP4) s = ldexpf(1.0f, (int)sb - 127);
+    else if constexpr (FMT == RAZER_W) { s = (float)sf_val<1>(sb & 0x3F); v = p.special[sb >> 6]; }
+    else { s = (float)sf_val<0>(sb & 0x7F); v = (sb & 0x80) ? -5.0f : 5.0f; }
+    float out[L];
+    static_for<0, L / 2>([&](auto ic) {
+      constexpr int b = decltype(ic)::value;
+      auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, b);
+      float q0 = v2[0] * s, q1 = v2[1] * s;  // exact (at most 8 significant bits)
+      if (FMT == RAZER_A || FMT == RAZER_W) {
+        if (((packed >> (8 * b)) & 15u) == 8u) q0 = v * s;
+        if (((packed >> (8 * b + 4)) & 15u) == 8u) q1 = v * s;
+      }
+      out[2 * b] = q0 * g;
+      out[2 * b + 1] = q1 * g;
+    });
+    if (p.out_bf16) {
+      uint16_t* dst = (uint16_t*)p.out + r * p.ld_out + j0;
+      uint32_t w[L / 2];
+#pragma unroll
+      for (int i = 0; i < L; i += 2) {
+        uint32_t a = fbits(out[i]), b = fbits(out[i + 1]);
+        a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;  // RNE to bf16 (finite)
+        b = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+        w[i / 2] = a | (b << 16);
+      }
+      if constexpr (L == 8) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+      else *(uint2*)dst = make_uint2(w[0], w[1]);
+    } else {
+      float* dst = (float*)p.out + r * p.ld_out + j0;
+#pragma unroll
+      for (int i = 0; i < L; i += 4) *(float4*)(dst + i) = make_float4(out[i], out[i + 1], out[i + 2], out[i + 3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- channel scale
+// MACaQ section 3: t_j = (rms_j(W) / rms_j(X))^alpha; 64 columns per
+// workgroup, 4 row slices combined in a fixed order
+__device__ __forceinline__ double load_any(const void* base, int bf16, int64_t idx) {
+  if (bf16) return (double)bitsf((uint32_t)((const uint16_t*)base)[idx] << 16);
+  return (double)((const float*)base)[idx];
+}
+
+__global__ __launch_bounds__(kThreads) void channel_scale_kernel(ChanScaleParams p) {
+  __shared__ double part[2][4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + tx;
+  double sx = 0.0, sw = 0.0;
+  if (j < p.cols) {
+    for (int64_t i = ty; i < p.rows_x; i += 4) { double v = load_any(p.x, p.x_bf16, i * p.ldx + j); sx += v * v; }
+    for (int64_t i = ty; i < p.rows_w; i += 4) { double v = load_any(p.w, p.w_bf16, i * p.ldw + j); sw += v * v; }
+  }
+  part[0][ty][tx] = sx;
+  part[1][ty][tx] = sw;
+  __syncthreads();
+  if (ty == 0 && j < p.cols) {
+    double X = (part[0][0][tx] + part[0][1][tx]) + (part[0][2][tx] + part[0][3][tx]);
+    double W = (part[1][0][tx] + part[1][1][tx]) + (part[1][2][tx] + part[1][3][tx]);
+    double rx = sqrt(X / (double)p.rows_x), rw = sqrt(W / (double)p.rows_w);
+    double tj = (rx == 0.0 || rw == 0.0) ? 1.0 : pow(rw / rx, p.alpha);
+    float tf = (float)tj;
+    p.t[j] = tf;
+    p.r[j] = 1.0f / tf;
+  }
+}
+
+int grid_for(int64_t work_items) {
+  int64_t blocks = (work_items + kThreads - 1) / kThreads;
+  const int64_t cap = 256 * 16;  // 16 workgroups per CU on 256 CUs
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+template <int FMT, int B, int RULE>
+hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
+  constexpr int L = (B == 4) ? 4 : 8;
+  int grid = grid_for(p.rows * (p.cols / L));
+  if (bf16) hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int FMT, int RULE>
+hipError_t launch_q2(int block, bool bf16, const QuantParams& p, hipStream_t s) {
+  switch (block) {
+    case 4: return launch_q3<FMT, 4, RULE>(bf16, p, s);
+    case 8: return launch_q3<FMT, 8, RULE>(bf16, p, s);
+    case 16: return launch_q3<FMT, 16, RULE>(bf16, p, s);
+    default: return launch_q3<FMT, 32, RULE>(bf16, p, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantParams& p,
+                           hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  const bool bf16 = p.x_bf16 != 0;
+  if (gmode == G_AUTO) {
+    hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
+    if (p.cols % 8 == 0) {
+      int grid = grid_for(p.rows * (p.cols / 8));
+      if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+      int grid = grid_for(p.rows * (p.cols / 4));
+      if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(amax4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+    }
+    hipLaunchKernelGGL(finalize_global_kernel, dim3(1), dim3(1), 0, s, p.global,
+                       fmt == RAZER_W ? 180.0f : 2688.0f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (fmt) {
+    case MXFP4: return launch_q3<MXFP4, 32, ABSMAX>(bf16, p, s);
+    case RAZER_A: return launch_q2<RAZER_A, ABSMAX>(block, bf16, p, s);
+    case RAZER_W: return launch_q2<RAZER_W, ABSMAX>(block, bf16, p, s);
+    default:
+      if (rule == FOUR6) return launch_q2<NVFP4, FOUR6>(block, bf16, p, s);
+      if (rule == BRUTE) return launch_q2<NVFP4, BRUTE>(block, bf16, p, s);
+      return launch_q2<NVFP4, ABSMAX>(block, bf16, p, s);
+  }
+}
+
+hipError_t launch_dequantize(int fmt, int block, const DequantParams& p, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  const int L = (block == 4) ? 4 : 8;
+  int grid = grid_for(p.rows * (p.cols / L));
+#define FP4Q_DQ(F, BB) hipLaunchKernelGGL((dequantize_kernel<F, BB>), dim3(grid), dim3(kThreads), 0, s, p)
+  switch (fmt) {
+    case MXFP4: FP4Q_DQ(MXFP4, 32); break;
+    case NVFP4:
+      if (block == 4) FP4Q_DQ(NVFP4, 4); else if (block == 8) FP4Q_DQ(NVFP4, 8);
+      else if (block == 16) FP4Q_DQ(NVFP4, 16); else FP4Q_DQ(NVFP4, 32);
+      break;
+    case RAZER_A:
+      if (block == 4) FP4Q_DQ(RAZER_A, 4); else if (block == 8) FP4Q_DQ(RAZER_A, 8);
+      else if (block == 16) FP4Q_DQ(RAZER_A, 16); else FP4Q_DQ(RAZER_A, 32);
+      break;
+    default:
+      if (block == 4) FP4Q_DQ(RAZER_W, 4); else if (block == 8) FP4Q_DQ(RAZER_W, 8);
+      else if (block == 16) FP4Q_DQ(RAZER_W, 16); else FP4Q_DQ(RAZER_W, 32);
+      break;
+  }
+#undef FP4Q_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s) {
+  int grid = (int)((p.cols + 63) / 64);
+  hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp4q

@@ -1,0 +1,195 @@
+"""GPU parity of fp4q_gemm_w4a4 against the CPU oracle (binary64
+accumulation): relative Frobenius error <= 1e-3 (the W4A4 tolerance), and
+bit-equality in the regime where every partial sum is exact in FP32.
+
+The GEMM inputs are produced by the oracle quantizer (never by the HIP
+quantizer).  At full workload sizes the GPU GEMM consumes a buffer whose
+sampled rows come from the oracle; only entries that depend on those rows
+alone are compared."""
+import numpy as np
+import pytest
+
+import datagen
+import oracle as O
+from tests.gpu_util import case, dev, host, rel_fro, scalar_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+SPECIAL = datagen.RAZER_SPECIAL
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_scaled_fp4_e4m3_amd as B
+    return B
+
+
+def oquant(x, fmt, rule=O.ABSMAX, gmode=O.G_AUTO, special=None):
+    block = 32 if fmt == "mxfp4" else 16
+    if fmt == "mxfp4":
+        gmode = O.G_NONE
+    return O.quantize(x, fmt, block, rule, gmode, special=special)
+
+
+def gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, special, out_dtype="f32", ldc_pad=0):
+    import torch
+    M, N = ca.shape[0], cw.shape[0]
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    per16 = 4 if out_dtype == "f32" else 8  # row pitch must be a multiple of 16 bytes
+    ld = -(-(N + ldc_pad) // per16) * per16
+    out = torch.empty((M, ld), dtype=dt, device="cuda")
+    c = out[:, :N]
+    B.gemm(fa, dev(ca), dev(sa), scalar_dev(ga), fw, dev(cw), dev(sw), scalar_dev(gw), special, out=c)
+    torch.cuda.synchronize()
+    r = host(c)
+    if out_dtype != "f32":
+        r = datagen.bf16_bits_to_f32(r)
+    return r
+
+
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w"), ("razer_a", "nvfp4"),
+                                   ("nvfp4", "razer_w"), ("nvfp4", "razer_a"), ("mxfp4", "mxfp4")])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (100, 130, 96), (1, 17, 160), (133, 67, 32), (7, 300, 544)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_small(B, fa, fw, M, N, K, out_dtype):
+    if fa == "mxfp4" and K % 32:
+        pytest.skip("MXFP4 needs K % 32 == 0")
+    a = datagen.student_t((M, K), 500 + M, 4.0)
+    w = datagen.normal((N, K), 600 + N, 0.02)
+    sp = SPECIAL if fw == "razer_w" else None
+    ca, sa, ga = oquant(a, fa)
+    cw, sw, gw = oquant(w, fw, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, M, N, K)
+    case(f"gemm {fa}x{fw} {M}x{N}x{K} {out_dtype}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp, out_dtype, ldc_pad=8)
+    tol = TOL if out_dtype == "f32" else 8e-3  # bf16 output rounding (2^-9 relative)
+    assert rel_fro(got, ref) <= tol
+
+
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("mxfp4", "mxfp4"), ("razer_a", "razer_w")])
+def test_gemm_exact_regime_bitwise(B, fa, fw):
+    # g = 1, every block scale 1 (E4M3 code 56, E8M0 127, E3M3 code 24), K <= 256:
+    # every partial sum is a multiple of 2^-2 below 2^14, exact in FP32, so the
+    # result does not depend on the summation order
+    M, N, K = 48, 80, 256
+    g = datagen.rng(7)
+    grid = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    a = g.choice(grid, (M, K)).astype(np.float32)
+    w = g.choice(grid, (N, K)).astype(np.float32)
+    bs = 32 if fa == "mxfp4" else 16
+    a[:, ::bs] = 6.0
+    w[:, ::bs] = -6.0
+    sp = SPECIAL if fw == "razer_w" else None
+    if fa == "mxfp4":
+        a[:, ::bs] = 4.0  # max in [4, 8) gives E = 0
+        w[:, ::bs] = -4.0
+    ca, sa, ga = O.quantize(a, fa, bs, O.ABSMAX, O.G_NONE)
+    cw, sw, gw = O.quantize(w, fw, bs, O.ABSMAX, O.G_NONE, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, M, N, K)
+    case(f"gemm exact {fa}x{fw}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp)
+    assert np.array_equal(got, ref)
+
+
+def test_gemm_razer_special_codes_decode(B):
+    # a weight made of special values only: every W element is code 0x8
+    M, N, K = 32, 40, 64
+    a = datagen.normal((M, K), 800)
+    ca, sa, ga = oquant(a, "nvfp4")
+    sp = (2.5, -7.5, 5.0, -3.5)
+    w = np.tile(np.array([2.5, -7.5, 5.0, -3.5] * (K // 4), np.float32), (N, 1))
+    cw, sw, gw = O.quantize(w, "razer_w", 16, O.ABSMAX, O.G_NONE, special=sp)
+    ref = O.gemm_rows("nvfp4", ca, sa, ga, "razer_w", cw, sw, gw, sp, M, N, K)
+    case("gemm razer special-only weight")
+    got = gpu_gemm(B, "nvfp4", ca, sa, ga, "razer_w", cw, sw, gw, sp)
+    assert rel_fro(got, ref) <= TOL
+
+
+# ------------------------------------------------------------------ full-size workloads
+def spliced_gemm(B, fa, fw, a_src, w_src, a_rows, w_rows, a_fmt_args, w_fmt_args, special=None, out_bf16=False):
+    """GPU-quantize the full operands (fast), overwrite the sampled rows with the
+    oracle's quantization of those rows (oracle global scales used for both),
+    run the GPU GEMM and compare the entries (a_rows x w_rows) with the oracle."""
+    import torch
+    block = 32 if fa == "mxfp4" else 16
+
+    def prep(x_np, x_gpu, fmt, args, rows, sp):
+        rule, gmode, t, had = args
+        if gmode == "auto":
+            g = O.auto_global(O.transform(x_np, t, had), fmt)
+        else:
+            g = 1.0
+        gbuf = scalar_dev(g)
+        mode = "given" if gmode == "auto" else gmode
+        case(f"gemm operand quantize {fmt} {tuple(x_gpu.shape)}")
+        codes, scales, _ = B.quantize(x_gpu, fmt, block, rule, mode, chan_scale=dev(t) if t is not None else None,
+                                      hadamard=had, special=sp or (0.0,) * 4, global_=gbuf)
+        orule = {"absmax": O.ABSMAX, "4over6": O.FOUR_OVER_SIX}[rule]
+        oc, os_ = O.quantize_rows(O.transform(x_np[rows], t, had), fmt, block, orule, g, sp)
+        idx = torch.as_tensor(rows, device="cuda")
+        codes.index_copy_(0, idx, dev(oc))
+        scales.index_copy_(0, idx, dev(os_))
+        return codes, scales, g, oc, os_
+
+    ac, as_, ga, oac, oas = prep(*a_src, fa, a_fmt_args, a_rows, None)
+    wc, ws, gw, owc, ows = prep(*w_src, fw, w_fmt_args, w_rows, special)
+    M, N, K = ac.shape[0], wc.shape[0], 2 * ac.shape[1]
+    case(f"gemm full {fa}x{fw} {M}x{N}x{K}")
+    out = torch.empty((M, N), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
+    B.gemm(fa, ac, as_, scalar_dev(ga), fw, wc, ws, scalar_dev(gw), special, out=out)
+    torch.cuda.synchronize()
+    sub = out.index_select(0, torch.as_tensor(a_rows, device="cuda")).index_select(1, torch.as_tensor(w_rows, device="cuda"))
+    got = host(sub)
+    if out_bf16:
+        got = datagen.bf16_bits_to_f32(got)
+    ref = O.gemm_rows(fa, oac, oas, ga, fw, owc, ows, gw, special, len(a_rows), len(w_rows), K)
+    return got, ref
+
+
+def rows_of(n, k, seed):
+    idx = datagen.rng(seed).choice(n, size=min(k, n), replace=False)
+    return np.sort(np.concatenate([idx, [0, n - 1]])).astype(np.int64)
+
+
+def test_tiny_workload_full(B):
+    d = datagen.tiny()
+    ca, sa, _ = O.quantize(d["A"], "nvfp4", 16, O.ABSMAX, O.G_NONE)
+    for rule in (O.ABSMAX, O.FOUR_OVER_SIX, O.BRUTE):
+        cw, sw, _ = O.quantize(d["W"], "nvfp4", 16, rule, O.G_NONE)
+        ref = O.gemm_rows("nvfp4", ca, sa, 1.0, "nvfp4", cw, sw, 1.0, None, 64, 256, 256)
+        case(f"gemm tiny workload rule {rule}")
+        got = gpu_gemm(B, "nvfp4", ca, sa, 1.0, "nvfp4", cw, sw, 1.0, None)
+        assert rel_fro(got, ref) <= TOL
+
+
+def test_mxfp4_linear_workload(B):
+    d = datagen.mxfp4_linear()
+    t, r = O.channel_scale(d["X_bf16"], d["W"], 0.75)
+    got, ref = spliced_gemm(B, "mxfp4", "mxfp4", (d["X_bf16"], dev(d["X_bf16"], bf16=True)), (d["W"], dev(d["W"])),
+                            rows_of(4096, 24, 50), rows_of(14336, 96, 51),
+                            ("absmax", "none", t, 32), ("absmax", "none", r, 32))
+    assert rel_fro(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_razer_decode_workload(B, M):
+    d = datagen.razer_decode(M)
+    a = d["A_bf16"]
+    got, ref = spliced_gemm(B, "razer_a", "razer_w", (a, dev(a, bf16=True)), (d["W"], dev(d["W"])),
+                            np.arange(M, dtype=np.int64) if M <= 16 else rows_of(M, 16, 60), rows_of(17408, 256, 61),
+                            ("absmax", "auto", None, 0), ("absmax", "auto", None, 0), special=SPECIAL)
+    assert rel_fro(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("N", datagen.PREFILL_N)
+def test_prefill_workload(B, N):
+    a = datagen.prefill_act()
+    w = datagen.prefill_weight(N)
+    got, ref = spliced_gemm(B, "nvfp4", "nvfp4", (a, dev(a, bf16=True)), (w, dev(w)),
+                            rows_of(32768, 12, 70), rows_of(N, 64, 71),
+                            ("4over6", "auto", None, 0), ("4over6", "auto", None, 0), out_bf16=(N == 17408))
+    assert rel_fro(got, ref) <= (TOL if N != 17408 else 8e-3)
