@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one pass of the whole path over one batch of synthetic input:
+
+  prefill (default)  32768 x 5120 bf16 activations (Student-t, nu=4):
+                     online NVFP4 4-over-6 quantization with a calibrated
+                     (given) global scale, then the three projection W4A4
+                     GEMMs N = 10240, 17408, 5120 (K = 5120) against weights
+                     quantized offline (NVFP4, 4-over-6, auto global scale),
+                     bf16 output.
+  mxfp4_linear       4096 x 4096 bf16 activations with 8 outlier channels:
+                     channel scale + block-Hadamard + MXFP4 quantization, then
+                     the 4096 x 14336 x 4096 MXFP4 GEMM, fp32 output.
+  razer_decode       RaZeR-A quantization of M x 5120 activations (M = 128),
+                     then the GEMM against RaZeR-W weights 17408 x 5120.
+
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+Kernel times come from HIP events recorded on the stream the kernels run on
+(torch's current stream, which the library is handed).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp4": 10100.0}   # dense, published
+METRIC = "FP4 quantize GB/s (% HBM peak); W4A4 GEMM TFLOP/s (% MFMA peak)"
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def dev_bf16(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+# ---------------------------------------------------------------- workloads
+class Prefill:
+    name = "prefill_hybrid_layer"
+    M, K, NS = 32768, 5120, (10240, 17408, 5120)
+    compute_dtype = "f16"
+    gemm_kernel = "gemm_nv_kernel"
+    quant_kernel = "quantize_kernel"
+
+    def __init__(self, B):
+        import torch
+        import datagen
+        self.B = B
+        log("[bench] generating prefill activations and weights")
+        a = datagen.prefill_act(self.M, self.K)
+        self.x = dev_bf16(a)
+        # calibrated global scale for the online quantizer: the auto scale of a
+        # calibration slice (rows 0..4095), computed by the library itself
+        _, _, g = B.quantize(self.x[:4096], "nvfp4", 16, "4over6", "auto")
+        self.g_act = g
+        self.codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.scales = torch.empty((self.M, self.K // 16), dtype=torch.uint8, device="cuda")
+        self.w = []
+        for n in self.NS:
+            w = torch.from_numpy(datagen.prefill_weight(n, self.K)).cuda()
+            wc, ws, wg = B.quantize(w, "nvfp4", 16, "4over6", "auto")  # offline
+            del w
+            out = torch.empty((self.M, n), dtype=torch.bfloat16, device="cuda")
+            self.w.append((wc, ws, wg, out))
+        torch.cuda.synchronize()
+        self.gemm_flops = [2.0 * self.M * n * self.K for n in self.NS]
+        self.quant_bytes = self.M * self.K * 2 + self.M * self.K // 2 + self.M * self.K // 16
+
+    def config(self):
+        return {"workload": f"{self.name}_M{self.M}_K{self.K}_N{'-'.join(map(str, self.NS))}",
+                "quant": "nvfp4 block16 e4m3 4over6 given-global bf16-in", "gemm": "nvfp4 x nvfp4 -> bf16",
+                "M": self.M, "K": self.K, "N": list(self.NS)}
+
+    def step(self, ev=None):
+        B = self.B
+        if ev: ev.mark("q0")
+        B.quantize(self.x, "nvfp4", 16, "4over6", "given", global_=self.g_act, codes=self.codes, scales=self.scales)
+        if ev: ev.mark("q1")
+        for i, (wc, ws, wg, out) in enumerate(self.w):
+            B.gemm("nvfp4", self.codes, self.scales, self.g_act, "nvfp4", wc, ws, wg, out=out)
+            if ev: ev.mark(f"g{i}")
+
+
+class MxLinear:
+    name = "mxfp4_linear"
+    M, K, N = 4096, 4096, 14336
+    compute_dtype = "fp4"
+    gemm_kernel = "gemm_mx_kernel"
+    quant_kernel = "quantize_kernel"
+
+    def __init__(self, B):
+        import torch
+        import datagen
+        self.B = B
+        d = datagen.mxfp4_linear(self.M, self.K, self.N)
+        self.x = dev_bf16(d["X_bf16"])
+        w = torch.from_numpy(d["W"]).cuda()
+        self.t, r = B.channel_scale(self.x, w, 0.75)  # calibration
+        self.wc, self.ws, _ = B.quantize(w, "mxfp4", 32, "absmax", "none", chan_scale=r, hadamard=32)
+        del w
+        self.codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.scales = torch.empty((self.M, self.K // 32), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((self.M, self.N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self.NS = (self.N,)
+        self.gemm_flops = [2.0 * self.M * self.N * self.K]
+        self.quant_bytes = self.M * self.K * 2 + self.M * self.K // 2 + self.M * self.K // 32
+
+    def config(self):
+        return {"workload": f"{self.name}_M{self.M}_K{self.K}_N{self.N}",
+                "quant": "mxfp4 + channel scale + block-Hadamard 32, bf16-in", "gemm": "mxfp4 x mxfp4 -> f32",
+                "M": self.M, "K": self.K, "N": [self.N]}
+
+    def step(self, ev=None):
+        B = self.B
+        if ev: ev.mark("q0")
+        B.quantize(self.x, "mxfp4", 32, "absmax", "none", chan_scale=self.t, hadamard=32,
+                   codes=self.codes, scales=self.scales)
+        if ev: ev.mark("q1")
+        B.gemm("mxfp4", self.codes, self.scales, None, "mxfp4", self.wc, self.ws, None, out=self.out)
+        if ev: ev.mark("g0")
+
+
+class RazerDecode:
+    name = "razer_decode"
+    M, K, N = 128, 5120, 17408
+    compute_dtype = "f16"
+    gemm_kernel = "gemm_nv_kernel"
+    quant_kernel = "quantize_kernel"
+
+    def __init__(self, B, M=128):
+        import torch
+        import datagen
+        self.B = B
+        self.M = M
+        d = datagen.razer_decode(M, self.N, self.K)
+        self.x = dev_bf16(d["A_bf16"])
+        w = torch.from_numpy(d["W"]).cuda()
+        self.sp = datagen.RAZER_SPECIAL
+        self.wc, self.ws, self.wg = B.quantize(w, "razer_w", 16, "absmax", "auto", special=self.sp)
+        del w
+        self.codes = torch.empty((M, self.K // 2), dtype=torch.uint8, device="cuda")
+        self.scales = torch.empty((M, self.K // 16), dtype=torch.uint8, device="cuda")
+        self.g = torch.ones(1, dtype=torch.float32, device="cuda")
+        self.out = torch.empty((M, self.N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self.NS = (self.N,)
+        self.gemm_flops = [2.0 * M * self.N * self.K]
+        self.quant_bytes = M * self.K * 2 + M * self.K // 2 + M * self.K // 16
+
+    def config(self):
+        return {"workload": f"{self.name}_M{self.M}_K{self.K}_N{self.N}",
+                "quant": "razer_a block16 auto-global bf16-in", "gemm": "razer_a x razer_w -> f32",
+                "M": self.M, "K": self.K, "N": [self.N]}
+
+    def step(self, ev=None):
+        B = self.B
+        if ev: ev.mark("q0")
+        B.quantize(self.x, "razer_a", 16, "absmax", "auto", global_=self.g, codes=self.codes, scales=self.scales)
+        if ev: ev.mark("q1")
+        B.gemm("razer_a", self.codes, self.scales, self.g, "razer_w", self.wc, self.ws, self.wg, self.sp, out=self.out)
+        if ev: ev.mark("g0")
+
+
+WORKLOADS = {"prefill": Prefill, "mxfp4_linear": MxLinear, "razer_decode": RazerDecode}
+
+
+class Marks:
+    """HIP events on the current stream, named by position in the step"""
+
+    def __init__(self):
+        self.rec = []
+
+    def mark(self, name):
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(torch.cuda.current_stream())
+        self.rec.append((name, e))
+
+    def durations(self):
+        """ms between consecutive marks: quantize = q0->q1, gemm i = prev->g{i}"""
+        out = {}
+        for (n0, e0), (n1, e1) in zip(self.rec, self.rec[1:]):
+            if n1 == "q0":
+                continue
+            out.setdefault(n1, []).append(e0.elapsed_time(e1))
+        return out
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """The oracle, as it is, on a bounded sample of the same workload, single
+    thread; extrapolated linearly to one whole step."""
+    import datagen
+    import oracle as O
+    O.build()
+    K = wl.K
+    if isinstance(wl, Prefill):
+        rows = 256
+        a = datagen.prefill_act(rows, K)  # same distribution; a slice of the recipe
+        g = float(wl.g_act.item())
+        t0 = time.perf_counter()
+        O.quantize_rows(O.transform(a), "nvfp4", 16, O.FOUR_OVER_SIX, g)
+        tq = (time.perf_counter() - t0) / (rows * K)  # s per element
+        codes, scales = O.quantize_rows(O.transform(a[:2]), "nvfp4", 16, O.FOUR_OVER_SIX, g)
+        fa = fw = "nvfp4"
+        wsamp = [O.quantize_rows(datagen.normal((1, K), 12 + i, 0.02), "nvfp4", 16, O.FOUR_OVER_SIX, 1e-4)
+                 for i in range(len(wl.NS))]
+        sp = None
+    elif isinstance(wl, MxLinear):
+        rows = 256
+        a = datagen.mxfp4_linear(wl.M, wl.K, 16)["X_bf16"][:rows]
+        t = wl.t.cpu().numpy()
+        t0 = time.perf_counter()
+        O.quantize(a, "mxfp4", 32, O.ABSMAX, O.G_NONE, chan_scale=t, hadamard=32)
+        tq = (time.perf_counter() - t0) / (rows * K)
+        codes, scales, _ = O.quantize(a[:2], "mxfp4", 32, O.ABSMAX, O.G_NONE, chan_scale=t, hadamard=32)
+        fa = fw = "mxfp4"
+        wsamp = [O.quantize_rows(datagen.normal((1, K), 6, 0.02), "mxfp4", 32, O.ABSMAX, 1.0)]
+        sp = None
+    else:
+        rows = min(wl.M, 128)
+        a = datagen.razer_decode(wl.M, with_weight=False)["A_bf16"][:rows]
+        t0 = time.perf_counter()
+        O.quantize(a, "razer_a", 16, O.ABSMAX, O.G_AUTO)
+        tq = (time.perf_counter() - t0) / (rows * K)
+        codes, scales, _ = O.quantize(a[:2], "razer_a", 16, O.ABSMAX, O.G_AUTO)
+        fa, fw = "razer_a", "razer_w"
+        sp = datagen.RAZER_SPECIAL
+        wsamp = [O.quantize_rows(datagen.normal((1, K), 7, 0.02), "razer_w", 16, O.ABSMAX, 1e-4, sp)]
+    # GEMM: time one A row against a replicated sample of W rows until the budget is used
+    t_gemm_per_mac = []
+    for (wc1, ws1), n in zip(wsamp, wl.NS):
+        reps = 2048
+        wc = np.repeat(wc1, reps, axis=0)
+        ws = np.repeat(ws1, reps, axis=0)
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < budget_s / (2 * len(wl.NS)):
+            O.gemm_rows(fa, codes, scales, 1.0, fw, wc, ws, 1.0, sp, 2, reps, K, 0, 1)
+            done += reps * K
+        t_gemm_per_mac.append((time.perf_counter() - t0) / done)
+    t_step = tq * wl.M * K + sum(tm * wl.M * n * K for tm, n in zip(t_gemm_per_mac, wl.NS))
+    flops = sum(wl.gemm_flops)
+    return {
+        "value": flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"single-thread oracle: quantize of {rows} x {K} rows, GEMM of 1 activation row against "
+                   f"2048 weight rows per projection repeated for ~{budget_s / 2:.0f} s; per-element and per-MAC "
+                   f"times extrapolated linearly to the full step"),
+        "step_s_extrapolated": t_step,
+    }
+
+
+# ---------------------------------------------------------------- traffic from PMC runs
+def traffic_record(kernel_source: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, only if
+    they were taken from the current kernel source"""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "block_scaled_fp4_e4m3_amd", "csrc", kernel_source), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_e4m3_amd as B
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    wl = WORKLOADS[args.workload](B)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, synchronised on both sides
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-kernel durations over the same number of steps, events between launches
+    marks = Marks()
+    for _ in range(args.steps):
+        wl.step(marks)
+    torch.cuda.synchronize()
+    d = marks.durations()
+    q_ms = float(np.mean(d["q1"]))
+    g_ms = [float(np.mean(d[f"g{i}"])) for i in range(len(wl.NS))]
+
+    flops_step = sum(wl.gemm_flops)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.compute_dtype]
+    # dominant kernel: the GEMM; per launch = mean algorithmic FLOPs / mean duration
+    gemm_avg_ms = float(np.mean(g_ms))
+    gemm_avg_flops = float(np.mean(wl.gemm_flops))
+    achieved = gemm_avg_flops / (gemm_avg_ms * 1e-3) / 1e12
+    traffic = None
+    rec = traffic_record("gemm.hip")
+    if rec and rec.get("workload") == wl.config()["workload"]:
+        traffic = rec.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "kernel": wl.gemm_kernel, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "avg_launch_ms": round(gemm_avg_ms, 4), "algorithmic_flops_per_launch": gemm_avg_flops}
+    quant_gbs = wl.quant_bytes / (q_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.compute_dtype,
+        "data": "synthetic",
+        "config": wl.config(),
+        "quantize": {"kernel": wl.quant_kernel, "avg_launch_ms": round(q_ms, 4), "bytes": wl.quant_bytes,
+                     "GB/s": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4)},
+        "gemm": [{"N": n, "avg_launch_ms": round(t, 4), "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1),
+                  "frac": round(f / (t * 1e-3) / 1e12 / peak, 4)} for n, t, f in zip(wl.NS, g_ms, wl.gemm_flops)],
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out))
+    sys.stdout.flush()
+
+
+if __name__ == "__main__":
+    main()
