@@ -133,7 +133,9 @@ fp4q_status fp4q_gemm_w4a4(fp4q_format fa, const uint8_t* a_codes, const uint8_t
   if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
   if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
   const int64_t block = fa == FP4Q_MXFP4 ? 32 : 16;
-  if (M < 0 || N < 0 || K <= 0 || K % block != 0 || ldc < N) return FP4Q_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || K % block != 0 || K > (int64_t(1) << 24) || ldc < N) return FP4Q_ERR_SHAPE;
+  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  if (tiles_n > 0 && tiles_m > INT32_MAX / tiles_n) return FP4Q_ERR_SHAPE;
   if (fw == FP4Q_NVFP4_RAZER_W)
     for (int i = 0; i < 4; ++i)
       if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;

@@ -10,14 +10,14 @@
 // row) and per-block scale bytes, K contiguous ("NT" layout).
 //
 // Tiling.  A workgroup of 4 waves computes a 256 x 256 tile; each wave owns a
-// 128 x 128 sub-tile as 4 x 4 MFMA 32x32 accumulators (256 FP32 per lane).
-// K advances in stages of 128 elements: the packed codes (64 bytes per row)
-// and scale bytes of both operands are loaded with coalesced 16-byte global
-// loads into registers, written to one of two LDS buffers (row stride 80
-// bytes, which keeps ds_read_b128 of 32 consecutive rows free of bank
-// conflicts), and read back per wave while the next stage's loads are in
-// flight.  Workgroup ids are remapped so that each XCD works on a contiguous,
-// grouped range of tiles and its L2 sees shared operand panels.
+// 128 x 128 sub-tile as 4 x 4 MFMA 32x32 accumulators (256 FP32 per lane, in
+// the accumulation registers).  K advances in stages of 128 elements: the
+// packed codes (64 bytes per row) and scale bytes of both operands are loaded
+// with 16-byte buffer loads into registers and written to one of two LDS
+// stage buffers in MFMA fragment order (below), so that every fragment read
+// is one lane-contiguous ds_read_b128.  Workgroup ids are remapped so that
+// each XCD works on a contiguous, grouped range of tiles and its L2 sees
+// shared operand panels.
 //
 // MXFP4: codes and E8M0 exponents go straight into the block-scaled FP4 MFMA
 // (V_MFMA_SCALE_F32_32X32X64_F8F6F4); a lane supplies the 32 codes of one MX
@@ -47,46 +47,55 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256;   // workgroup tile
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;          // tile rows per group in the tile order
+constexpr int BK = 128;             // K elements per stage
+constexpr int KB = BK / 2;          // code bytes per row per stage
+constexpr int CPR = KB / 16;        // 16-byte code chunks per row per stage
+constexpr int NCH = BM * CPR / kThreads;  // code chunks per thread per operand per stage
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 
-// Per-format stage geometry: K elements per stage, code bytes per row, LDS
-// row stride (padded by 16 bytes against bank conflicts), scale bytes per row.
-template <bool MX>
-struct Geo {
-  static constexpr int BLK = MX ? 32 : 16;    // elements per scale block
-  static constexpr int BK = 128;               // K elements per stage
-  static constexpr int KB = BK / 2;           // code bytes per row per stage
-  static constexpr int ROWB = KB + 16;        // LDS row stride
-  static constexpr int CPR = KB / 16;         // 16-byte chunks per row
-  static constexpr int NCH = BM * CPR / kThreads;  // chunks per thread per operand
-  static constexpr int NS = BK / BLK;         // scale bytes per row per stage
-  static constexpr int NKC = BK / 64;         // 64-element chunks per stage
-};
+// ---------------------------------------------------------------- LDS stage layout
+// One stage buffer: [A codes][W codes][A scales][W scales].
+//   codes: 256 rows x 64 bytes as 16-byte slots.  Row r = 32 g + r32, chunk
+//     c = 2 kc + kh (kc: 64-element chunk, kh: its half).  Slot
+//     128 g + 32 c + (r32 ^ 4c): the 64 lanes (r32, kh) of a fragment read of
+//     tile g, chunk kc touch 64 consecutive slots (one ds_read_b128 over a
+//     contiguous KiB), and the XOR keeps the stores, where 16 consecutive
+//     threads write 4 rows x 4 chunks, on 16 distinct slots mod 16.
+//   scales: one dword per (row, kh), dword slot 64 g + 32 kh + r32, holding
+//     the scale bytes lane (r32, kh) needs for the whole stage:
+//     NVFP4 family: blocks 2kh, 2kh+1 (chunk 0), 4+2kh, 5+2kh (chunk 1);
+//     MXFP4: blocks kh (chunk 0), 2+kh (chunk 1), then two zero bytes.
+constexpr int kCodeBytes = BM * KB;                              // 16 KiB
+constexpr int kScaleBytes = BM * 2 * 4;                          // 2 KiB
+constexpr int kBufBytes = 2 * kCodeBytes + 2 * kScaleBytes;      // 36 KiB
+constexpr int kNbuf = 2;
 
-template <bool MX>
-struct Smem {
-  using G = Geo<MX>;
-  uint8_t a[2][BM * G::ROWB];
-  uint8_t w[2][BN * G::ROWB];
-  uint8_t sa[2][BM * G::NS];
-  uint8_t sw[2][BN * G::NS];
-};
-
-// ---------------------------------------------------------------- decode
-// scale byte -> f16 bit pattern of scale * 2^-8 (E4M3) or scale * 2^-12 (E3M3)
-template <int F>
-__device__ __forceinline__ uint32_t scale_f16_bits(uint32_t sb) {
-  return (F == RAZER_W ? (sb & 0x3Fu) : (sb & 0x7Fu)) << 7;
+__device__ __forceinline__ int code_slot(int row, int c) {
+  return (row >> 5) * 128 + c * 32 + ((row & 31) ^ (c << 2));
 }
 
-template <int F>
-__device__ __forceinline__ half8 decode8(uint32_t codes, uint32_t s16bits, uint32_t sb, const float* wspecial) {
+// ---------------------------------------------------------------- decode
+// f16 bit patterns of scale * 2^-8 (E4M3) or scale * 2^-12 (E3M3) for the two
+// scale bytes of chunk KC in a stage scale dword, packed in the two halves
+template <int F, int KC>
+__device__ __forceinline__ uint32_t scale_pair_f16(uint32_t raw4) {
+  constexpr uint32_t m = (F == RAZER_W) ? 0x3Fu : 0x7Fu;
+  const uint32_t two = __builtin_amdgcn_perm(0u, raw4, KC ? 0x0C030C02u : 0x0C010C00u);
+  return (two & (m | (m << 16))) << 7;
+}
+
+// 8 codes -> 8 f16 values value * scale; H selects the block (half of scl2),
+// byte B of raw4 is the block's raw scale byte (RaZeR special selector)
+template <int F, int H, int B>
+__device__ __forceinline__ half8 decode8(uint32_t codes, uint32_t scl2, uint32_t raw4, const float* wspecial) {
   constexpr float kCvt = (F == RAZER_W) ? 4096.0f : 256.0f;
-  const _Float16 s16 = __builtin_bit_cast(_Float16, (uint16_t)s16bits);
+  const _Float16 s16 = __builtin_bit_cast(half2v, scl2)[H];
   const half2v s2 = {s16, s16};
   half8 out;
   static_for<0, 4>([&](auto ic) {
@@ -97,6 +106,7 @@ __device__ __forceinline__ half8 decode8(uint32_t codes, uint32_t s16bits, uint3
     out[2 * b + 1] = v[1];
   });
   if constexpr (F == RAZER_A || F == RAZER_W) {
+    const uint32_t sb = (raw4 >> (8 * B)) & 0xFFu;
     float v = (F == RAZER_A) ? ((sb & 0x80u) ? -5.0f : 5.0f) : wspecial[sb >> 6];
     const _Float16 vs = (_Float16)(v * kCvt) * s16;  // exact
 #pragma unroll
@@ -126,46 +136,84 @@ __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int& tm, int& 
 
 // ---------------------------------------------------------------- staging
 // Each thread moves NCH 16-byte chunks of codes per operand per stage (chunk
-// q = i * 256 + tid covers row q / CPR, bytes 16 * (q % CPR)) and the NS scale
-// bytes of row tid.  Row indices past M (N) are clamped to the last row; those
-// rows are computed and never stored.
+// q = i * 256 + tid covers row q / 4, bytes 16 * (q % 4)) and the scale bytes
+// of row tid.  Row indices past M (N) are clamped to the last row; those rows
+// are computed and never stored.
 template <bool MX>
 struct Loader {
-  using G = Geo<MX>;
+  static constexpr int BLK = MX ? 32 : 16;   // elements per scale block
+  static constexpr int NS = BK / BLK;        // scale bytes per row per stage
   const uint8_t* a_base;     // codes of the tile's first row
   const uint8_t* w_base;
   const uint8_t* sa_row;     // scales of this thread's row
   const uint8_t* sw_row;
-  uint32_t a_off[G::NCH], w_off[G::NCH];  // byte offsets of the chunks at k = 0
+  __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;  // buffer views of the same
+  uint32_t a_off[NCH], w_off[NCH];  // byte offsets of the chunks at k = 0
+  uint32_t sa_off, sw_off;          // byte offsets of this thread's scale rows
   int64_t rowbytes, nblocks;
   bool vec_scales;
 
   __device__ void init(const GemmParams& p, int64_t m0, int64_t n0) {
     const int t = threadIdx.x;
     rowbytes = p.K / 2;
-    nblocks = p.K / G::BLK;
+    nblocks = p.K / BLK;
     a_base = p.a_codes + m0 * rowbytes;
     w_base = p.w_codes + n0 * rowbytes;
 #pragma unroll
-    for (int i = 0; i < G::NCH; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int q = i * kThreads + t;
-      const int row = q / G::CPR, c16 = q % G::CPR;
-      const int64_t ra = min((int64_t)row, p.M - 1 - m0), rw = min((int64_t)row, p.N - 1 - n0);
-      a_off[i] = (uint32_t)(ra * rowbytes + 16 * c16);
-      w_off[i] = (uint32_t)(rw * rowbytes + 16 * c16);
+      const int row = q / CPR, c16 = q % CPR;
+      const int64_t rA = min((int64_t)row, p.M - 1 - m0), rW = min((int64_t)row, p.N - 1 - n0);
+      a_off[i] = (uint32_t)(rA * rowbytes + 16 * c16);
+      w_off[i] = (uint32_t)(rW * rowbytes + 16 * c16);
     }
-    sa_row = p.a_scales + min(m0 + t, p.M - 1) * nblocks;
-    sw_row = p.w_scales + min(n0 + t, p.N - 1) * nblocks;
-    vec_scales = (nblocks % G::NS == 0) && ((((uintptr_t)p.a_scales | (uintptr_t)p.w_scales) & 3u) == 0);
+    const uint8_t* sa0 = p.a_scales + m0 * nblocks;
+    const uint8_t* sw0 = p.w_scales + n0 * nblocks;
+    sa_off = (uint32_t)(min((int64_t)t, p.M - 1 - m0) * nblocks);
+    sw_off = (uint32_t)(min((int64_t)t, p.N - 1 - n0) * nblocks);
+    sa_row = sa0 + sa_off;
+    sw_row = sw0 + sw_off;
+    ra = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, -1, (int)kRsrcWord3);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)w_base, (short)0, -1, (int)kRsrcWord3);
+    rsa = __builtin_amdgcn_make_buffer_rsrc((void*)sa0, (short)0, -1, (int)kRsrcWord3);
+    rsw = __builtin_amdgcn_make_buffer_rsrc((void*)sw0, (short)0, -1, (int)kRsrcWord3);
+    vec_scales = (nblocks % NS == 0) && ((((uintptr_t)p.a_scales | (uintptr_t)p.w_scales) & 3u) == 0);
   }
 };
 
 template <bool MX>
 struct Stage {
-  static constexpr int NSW = Geo<MX>::NS / 4;  // 32-bit words of scale bytes per row
-  uint4 a[Geo<MX>::NCH], w[Geo<MX>::NCH];
+  static constexpr int NSW = Loader<MX>::NS / 4;  // 32-bit words of scale bytes per row
+  uint4 a[NCH], w[NCH];
   uint32_t sa[NSW], sw[NSW];
 };
+
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) {
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// a stage entirely inside K with word-aligned scale rows: buffer loads whose
+// only per-stage change is the scalar offset
+template <bool MX>
+__device__ __forceinline__ void load_fast(const Loader<MX>& L, int64_t k0, Stage<MX>& s) {
+  const int kb = (int)(k0 / 2), b0 = (int)(k0 / Loader<MX>::BLK);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    s.a[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.ra, (int)L.a_off[i], kb, 0));
+    s.w[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.rw, (int)L.w_off[i], kb, 0));
+  }
+  if constexpr (MX) {
+    s.sa[0] = __builtin_amdgcn_raw_buffer_load_b32(L.rsa, (int)L.sa_off, b0, 0);
+    s.sw[0] = __builtin_amdgcn_raw_buffer_load_b32(L.rsw, (int)L.sw_off, b0, 0);
+  } else {
+    const auto va = __builtin_amdgcn_raw_buffer_load_b64(L.rsa, (int)L.sa_off, b0, 0);
+    const auto vw = __builtin_amdgcn_raw_buffer_load_b64(L.rsw, (int)L.sw_off, b0, 0);
+    s.sa[0] = va[0];
+    s.sa[1] = va[1];
+    s.sw[0] = vw[0];
+    s.sw[1] = vw[1];
+  }
+}
 
 // NS scale bytes of one row from block b0; blocks past the row read as 0
 template <int NS>
@@ -182,30 +230,6 @@ __device__ __forceinline__ void scales_bytes(const uint8_t* row, int64_t b0, int
   }
 }
 
-// a stage entirely inside K: unconditional 16-byte loads
-template <bool MX>
-__device__ __forceinline__ void load_full(const Loader<MX>& L, int64_t k0, Stage<MX>& s) {
-  using G = Geo<MX>;
-  const uint8_t* ab = L.a_base + k0 / 2;
-  const uint8_t* wb = L.w_base + k0 / 2;
-#pragma unroll
-  for (int i = 0; i < G::NCH; ++i) {
-    s.a[i] = *(const uint4*)(ab + L.a_off[i]);
-    s.w[i] = *(const uint4*)(wb + L.w_off[i]);
-  }
-  const int64_t b0 = k0 / G::BLK;
-  if (L.vec_scales) {
-#pragma unroll
-    for (int w = 0; w < G::NS / 4; ++w) {
-      s.sa[w] = *(const uint32_t*)(L.sa_row + b0 + 4 * w);
-      s.sw[w] = *(const uint32_t*)(L.sw_row + b0 + 4 * w);
-    }
-  } else {
-    scales_bytes<G::NS>(L.sa_row, b0, L.nblocks, s.sa);
-    scales_bytes<G::NS>(L.sw_row, b0, L.nblocks, s.sw);
-  }
-}
-
 // the last, partial stage: bytes past the row end read as zero codes
 __device__ __forceinline__ uint4 load_codes_tail(const uint8_t* p, int64_t off, int64_t rowbytes) {
   uint4 v = make_uint4(0, 0, 0, 0);
@@ -218,122 +242,312 @@ __device__ __forceinline__ uint4 load_codes_tail(const uint8_t* p, int64_t off, 
   return v;
 }
 
+// any stage: per-chunk bounds and byte-wise scale loads
 template <bool MX>
-__device__ __forceinline__ void load_tail(const Loader<MX>& L, int64_t k0, Stage<MX>& s) {
-  using G = Geo<MX>;
+__device__ __forceinline__ void load_any(const Loader<MX>& L, int64_t k0, Stage<MX>& s) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < G::NCH; ++i) {
-    const int c16 = (i * kThreads + t) % G::CPR;
+  for (int i = 0; i < NCH; ++i) {
+    const int c16 = (i * kThreads + t) % CPR;
     const int64_t off = k0 / 2 + 16 * c16;  // offset within the row
     s.a[i] = load_codes_tail(L.a_base + k0 / 2 + L.a_off[i], off, L.rowbytes);
     s.w[i] = load_codes_tail(L.w_base + k0 / 2 + L.w_off[i], off, L.rowbytes);
   }
-  scales_bytes<G::NS>(L.sa_row, k0 / G::BLK, L.nblocks, s.sa);
-  scales_bytes<G::NS>(L.sw_row, k0 / G::BLK, L.nblocks, s.sw);
+  scales_bytes<Loader<MX>::NS>(L.sa_row, k0 / Loader<MX>::BLK, L.nblocks, s.sa);
+  scales_bytes<Loader<MX>::NS>(L.sw_row, k0 / Loader<MX>::BLK, L.nblocks, s.sw);
 }
 
+// stage -> LDS buffer at `buf` in fragment order
 template <bool MX>
-__device__ __forceinline__ void store_stage(Smem<MX>& sm, int buf, const Stage<MX>& s) {
-  using G = Geo<MX>;
+__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage<MX>& s) {
   const int t = threadIdx.x;
+  uint8_t* ca = buf + code_slot(t / CPR, t % CPR) * 16;
 #pragma unroll
-  for (int i = 0; i < G::NCH; ++i) {
-    const int q = i * kThreads + t;
-    const int row = q / G::CPR, c16 = q % G::CPR;
-    *(uint4*)&sm.a[buf][row * G::ROWB + 16 * c16] = s.a[i];
-    *(uint4*)&sm.w[buf][row * G::ROWB + 16 * c16] = s.w[i];
+  for (int i = 0; i < NCH; ++i) {  // chunk i holds rows 64 i + t / 4: slot + 256 i
+    *(uint4*)(ca + i * 4096) = s.a[i];
+    *(uint4*)(ca + kCodeBytes + i * 4096) = s.w[i];
   }
-#pragma unroll
-  for (int w = 0; w < G::NS / 4; ++w) {
-    *(uint32_t*)&sm.sa[buf][t * G::NS + 4 * w] = s.sa[w];
-    *(uint32_t*)&sm.sw[buf][t * G::NS + 4 * w] = s.sw[w];
+  uint32_t a0, a1, w0, w1;
+  if constexpr (MX) {
+    a0 = __builtin_amdgcn_perm(0u, s.sa[0], 0x0C0C0200u);
+    a1 = __builtin_amdgcn_perm(0u, s.sa[0], 0x0C0C0301u);
+    w0 = __builtin_amdgcn_perm(0u, s.sw[0], 0x0C0C0200u);
+    w1 = __builtin_amdgcn_perm(0u, s.sw[0], 0x0C0C0301u);
+  } else {
+    a0 = __builtin_amdgcn_perm(s.sa[1], s.sa[0], 0x05040100u);
+    a1 = __builtin_amdgcn_perm(s.sa[1], s.sa[0], 0x07060302u);
+    w0 = __builtin_amdgcn_perm(s.sw[1], s.sw[0], 0x05040100u);
+    w1 = __builtin_amdgcn_perm(s.sw[1], s.sw[0], 0x07060302u);
   }
+  uint32_t* sc = (uint32_t*)(buf + 2 * kCodeBytes) + (t >> 5) * 64 + (t & 31);
+  sc[0] = a0;
+  sc[32] = a1;
+  sc[kScaleBytes / 4] = w0;
+  sc[kScaleBytes / 4 + 32] = w1;
+}
+
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its global loads in flight
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// interleave: one MFMA, then n VALU instructions, `count` times
-template <int COUNT, int NVALU>
-__device__ __forceinline__ void interleave_mfma_valu() {
-  static_for<0, COUNT>([&](auto) {
+// Scheduling of one MFMA step (16 MFMAs): each MFMA is followed by up to one
+// LDS write, one global load and one LDS read (for the first NDSW / NVMEM /
+// NDSR MFMAs) and NVALU vector instructions; nothing crosses the step.
+template <int NDSW, int NVMEM, int NDSR, int NVALU>
+__device__ __forceinline__ void sched_step() {
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (k < NDSW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if constexpr (k < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if constexpr (k < NDSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
   });
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// ---------------------------------------------------------------- compute on one stage
-// NVFP4 family: 2 chunks of 64 x 4 MFMA steps; the decode of step s+1 is
-// interleaved with the 16 MFMAs of step s
+// ---------------------------------------------------------------- NVFP4-family K loop
+// Per-wave registers: the codes of the stage's two chunks for the wave's 4 A
+// row tiles and 4 W column tiles, the stage scale dwords, and the f16 scale
+// pairs of each chunk.
+struct NvRegs {
+  uint4 ca0[4], cw0[4], ca1[4], cw1[4];
+  uint32_t ra[4], rw[4];     // stage scale dwords (read one stage ahead)
+  uint32_t qa[4], qw[4];     // the current stage's dwords for chunk 1 (RaZeR)
+  uint32_t pa0[4], pw0[4], pa1[4], pw1[4];
+};
+
+struct NvAddr {   // per-lane LDS byte offsets within a stage buffer
+  uint32_t a[2], w[2];  // code fragment of tile 0, chunk kc
+  uint32_t sa, sw;      // scale dword of tile 0
+};
+
+__device__ __forceinline__ void read_codes(const uint8_t* buf, const NvAddr& ad, int kc, uint4 (&ca)[4], uint4 (&cw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ca[i] = *(const uint4*)(buf + ad.a[kc] + i * 2048);
+    cw[i] = *(const uint4*)(buf + ad.w[kc] + i * 2048);
+  }
+}
+
+__device__ __forceinline__ void read_scales(const uint8_t* buf, const NvAddr& ad, uint32_t (&ra)[4], uint32_t (&rw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = *(const uint32_t*)(buf + ad.sa + i * 256);
+    rw[i] = *(const uint32_t*)(buf + ad.sw + i * 256);
+  }
+}
+
+// decode of MFMA step J (0..3) of chunk KC: codes word J, scale block J / 2
+template <int FA, int FW, int KC, int J>
+__device__ __forceinline__ void decode_step(const uint4 (&ca)[4], const uint4 (&cw)[4], const uint32_t (&pa)[4],
+                                            const uint32_t (&pw)[4], const uint32_t (&qa)[4], const uint32_t (&qw)[4],
+                                            const float* wspecial, half8 (&a)[4], half8 (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = decode8<FA, J / 2, 2 * KC + J / 2>(u4_get(ca[i], J), pa[i], qa[i], nullptr);
+    b[i] = decode8<FW, J / 2, 2 * KC + J / 2>(u4_get(cw[i], J), pw[i], qw[i], wspecial);
+  }
+}
+
+__device__ __forceinline__ void mfma_step(const half8 (&a)[4], const half8 (&b)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// The K loop, software-pipelined across stages.  A stage is 128 elements =
+// 2 chunks x 4 MFMA steps; stage x lives in LDS buffer x % 2.  While the 16
+// MFMAs of step t run, the wave decodes step t + 1 (step 7 decodes the first
+// step of the next stage).  Within stage s:
+//   step 0: store the registers holding stage s+1 into its LDS buffer
+//           (last read during stage s-2, before the barrier of stage s-1);
+//   step 1: issue the global loads of stage s+2 into those registers;
+//   steps 0-1: f16 scale pairs of chunk 1;  end of step 2: LDS barrier;
+//   step 3: read stage s+1's scale dwords and chunk-0 codes;
+//   steps 4-5: f16 scale pairs of stage s+1 chunk 0;
+//   step 7: read stage s+1's chunk-1 codes.
+// Every LDS read is used at least three steps after it is issued and every
+// global load about seven steps after.
 template <int FA, int FW>
-__device__ __forceinline__ void compute_stage_nv(const Smem<false>& sm, int buf, int wm, int wn,
-                                                 const float* wspecial, f32x16 (&acc)[4][4]) {
-  using G = Geo<false>;
+__device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
+                                        f32x16 (&acc)[4][4]) {
+  constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);  // special values need raw scale bytes
+  Loader<false> L;
+  L.init(p, m0, n0);
+  const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
-  uint4 ca[2][4], cw[2][4];
-  uint32_t sa[2][4], sw[2][4];
+  NvAddr ad;
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + 32 * i + r32, rw = wn * 128 + 32 * i + r32;
-      ca[kc][i] = *(const uint4*)&sm.a[buf][ra * G::ROWB + kc * 32 + kh * 16];
-      cw[kc][i] = *(const uint4*)&sm.w[buf][rw * G::ROWB + kc * 32 + kh * 16];
-      sa[kc][i] = *(const uint16_t*)&sm.sa[buf][ra * G::NS + kc * 4 + kh * 2];
-      sw[kc][i] = *(const uint16_t*)&sm.sw[buf][rw * G::NS + kc * 4 + kh * 2];
-    }
-  half8 da[2][4], db[2][4];
-  auto decode_step = [&](int step, half8 (&a)[4], half8 (&b)[4]) {
-    const int kc = step >> 2, j = step & 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t sba = (sa[kc][i] >> (8 * (j >> 1))) & 0xFFu;
-      const uint32_t sbw = (sw[kc][i] >> (8 * (j >> 1))) & 0xFFu;
-      a[i] = decode8<FA>(u4_get(ca[kc][i], j), scale_f16_bits<FA>(sba), sba, nullptr);
-      b[i] = decode8<FW>(u4_get(cw[kc][i], j), scale_f16_bits<FW>(sbw), sbw, wspecial);
-    }
+  for (int kc = 0; kc < 2; ++kc) {
+    const int c = 2 * kc + kh;
+    const uint32_t o = (uint32_t)(c * 32 + (r32 ^ (c << 2))) * 16;
+    ad.a[kc] = o + wm * 4 * 2048;
+    ad.w[kc] = o + kCodeBytes + wn * 4 * 2048;
+  }
+  ad.sa = 2 * kCodeBytes + (wm * 4 * 64 + lane) * 4;
+  ad.sw = 2 * kCodeBytes + kScaleBytes + (wn * 4 * 64 + lane) * 4;
+
+  Stage<false> st;
+  auto gload = [&](int64_t stg) {
+    if (stg < nfull && L.vec_scales) load_fast<false>(L, stg * BK, st);
+    else load_any<false>(L, stg * BK, st);
   };
-  decode_step(0, da[0], db[0]);
-  static_for<0, 8>([&](auto sc) {
-    constexpr int step = decltype(sc)::value;
-    constexpr int cur = step & 1;
-    if constexpr (step + 1 < 8) decode_step(step + 1, da[cur ^ 1], db[cur ^ 1]);
+  gload(0);
+  store_stage<false>(smem, st);
+  if (nstages > 1) gload(1);
+  lds_barrier();
+  NvRegs R;
+  read_scales(smem, ad, R.ra, R.rw);
+  read_codes(smem, ad, 0, R.ca0, R.cw0);
+  read_codes(smem, ad, 1, R.ca1, R.cw1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
+    R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
+  }
+  half8 da[2][4], db[2][4];
+  decode_step<FA, FW, 0, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[0], db[0]);
+
+  // FAST: stages s with s + 2 < nfull and word-aligned scales (branch-free);
+  // the others check whether stage s+1 / s+2 exist.  On the last stage the
+  // reads of the next stage read a stale buffer, which is harmless.
+  auto stage = [&](int64_t s, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const uint8_t* rbuf = smem + ((s + 1) & 1) * kBufBytes;
+    uint8_t* wbuf = smem + ((s + 1) & 1) * kBufBytes;
+    static_for<0, 8>([&](auto tc) {
+      constexpr int t = decltype(tc)::value, cur = t & 1;
+      if constexpr (t == 0) {
+        if (FAST || s + 1 < nstages) store_stage<false>(wbuf, st);
+      }
+      if constexpr (t == 1) {
+        if constexpr (FAST) load_fast<false>(L, (s + 2) * BK, st);
+        else if (s + 2 < nstages) gload(s + 2);
+      }
+      if constexpr (t == 0 || t == 1) {  // chunk-1 scale pairs, A at step 0, W at step 1
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[cur][i], db[cur][jj], acc[i][jj], 0, 0, 0);
-    if constexpr (step + 1 < 8) interleave_mfma_valu<16, 4>();
-  });
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (t == 0) {
+            R.pa1[i] = scale_pair_f16<FA, 1>(R.ra[i]);
+            if constexpr (RZ) R.qa[i] = R.ra[i];
+          } else {
+            R.pw1[i] = scale_pair_f16<FW, 1>(R.rw[i]);
+            if constexpr (RZ) R.qw[i] = R.rw[i];
+          }
+        }
+      }
+      if constexpr (t == 3) {
+        read_scales(rbuf, ad, R.ra, R.rw);
+        read_codes(rbuf, ad, 0, R.ca0, R.cw0);
+      }
+      if constexpr (t == 4 || t == 5) {  // next stage's chunk-0 scale pairs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (t == 4) R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
+          else R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
+        }
+      }
+      if constexpr (t == 7) read_codes(rbuf, ad, 1, R.ca1, R.cw1);
+      // decode of step t + 1
+      if constexpr (t < 3)
+        decode_step<FA, FW, 0, t + 1>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+      else if constexpr (t < 7)
+        decode_step<FA, FW, 1, t - 3>(R.ca1, R.cw1, R.pa1, R.pw1, R.qa, R.qw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+      else
+        decode_step<FA, FW, 0, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+      mfma_step(da[cur], db[cur], acc);
+      if constexpr (FAST) {
+        if constexpr (t == 0) sched_step<2 * NCH + 4, 0, 0, 5>();
+        else if constexpr (t == 1) sched_step<0, 2 * NCH + 2, 0, 5>();
+        else if constexpr (t == 3) sched_step<0, 0, 16, 4>();
+        else if constexpr (t == 4 || t == 5) sched_step<0, 0, 0, 5>();
+        else if constexpr (t == 7) sched_step<0, 0, 8, 4>();
+        else sched_step<0, 0, 0, 4>();
+      }
+      if constexpr (t == 2) lds_barrier();
+    });
+  };
+  int64_t s = 0;
+  if (L.vec_scales)
+    for (; s + 2 < nfull; ++s) stage(s, std::true_type{});
+  for (; s < nstages; ++s) stage(s, std::false_type{});
 }
 
-// MXFP4: 4 chunks of 64 per stage, 16 block-scaled MFMAs per chunk
-__device__ __forceinline__ void compute_stage_mx(const Smem<true>& sm, int buf, int wm, int wn,
-                                                 f32x16 (&acc)[4][4]) {
-  using G = Geo<true>;
-  const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int kc = 0; kc < G::NKC; ++kc) {
+// ---------------------------------------------------------------- MXFP4 K loop
+// 2 chunks of 64 per stage, 16 block-scaled MFMAs per chunk; the MFMA takes
+// the stage scale dword and selects the chunk's byte.
+__device__ __forceinline__ void compute_stage_mx(const uint8_t* buf, const NvAddr& ad, f32x16 (&acc)[4][4]) {
+  uint32_t sa[4], sw[4];
+  read_scales(buf, ad, sa, sw);
+  static_for<0, 2>([&](auto kcc) {
+    constexpr int kc = decltype(kcc)::value;
     uint4 ca[4], cw[4];
-    int sa[4], sw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + 32 * i + r32, rw = wn * 128 + 32 * i + r32;
-      ca[i] = *(const uint4*)&sm.a[buf][ra * G::ROWB + kc * 32 + kh * 16];
-      cw[i] = *(const uint4*)&sm.w[buf][rw * G::ROWB + kc * 32 + kh * 16];
-      sa[i] = sm.sa[buf][ra * G::NS + kc * 2 + kh];
-      sw[i] = sm.sw[buf][rw * G::NS + kc * 2 + kh];
-    }
+    read_codes(buf, ad, kc, ca, cw);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const i32x8 a = {(int)ca[i].x, (int)ca[i].y, (int)ca[i].z, (int)ca[i].w, 0, 0, 0, 0};
         const i32x8 b = {(int)cw[jj].x, (int)cw[jj].y, (int)cw[jj].z, (int)cw[jj].w, 0, 0, 0, 0};
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][jj], 4, 4, 0, sa[i], 0, sw[jj]);
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][jj], 4, 4, kc, (int)sa[i], kc,
+                                                                      (int)sw[jj]);
       }
+  });
+}
+
+__device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
+                                        f32x16 (&acc)[4][4]) {
+  Loader<true> L;
+  L.init(p, m0, n0);
+  const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
+  NvAddr ad;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int c = 2 * kc + kh;
+    const uint32_t o = (uint32_t)(c * 32 + (r32 ^ (c << 2))) * 16;
+    ad.a[kc] = o + wm * 4 * 2048;
+    ad.w[kc] = o + kCodeBytes + wn * 4 * 2048;
+  }
+  ad.sa = 2 * kCodeBytes + (wm * 4 * 64 + lane) * 4;
+  ad.sw = 2 * kCodeBytes + kScaleBytes + (wn * 4 * 64 + lane) * 4;
+  // stages entirely inside K run branch-free; the last stage may be partial
+  const int64_t nfull = p.K / BK;
+  const int64_t nstages = (p.K + BK - 1) / BK;
+  Stage<true> st;
+  if (nfull > 0 && L.vec_scales) load_fast<true>(L, 0, st);
+  else load_any<true>(L, 0, st);
+  store_stage<true>(smem, st);
+  lds_barrier();
+  int64_t s = 0;
+  if (L.vec_scales) {
+    for (; s + 1 < nfull; ++s) {          // next stage is a full one
+      const int buf = (int)(s & 1);
+      load_fast<true>(L, (s + 1) * BK, st);
+      compute_stage_mx(smem + buf * kBufBytes, ad, acc);
+      store_stage<true>(smem + (buf ^ 1) * kBufBytes, st);
+      lds_barrier();
+    }
+  }
+  for (; s < nstages; ++s) {
+    const int buf = (int)(s & 1);
+    const bool more = s + 1 < nstages;
+    if (more) {
+      if (s + 1 < nfull && L.vec_scales) load_fast<true>(L, (s + 1) * BK, st);
+      else load_any<true>(L, (s + 1) * BK, st);
+    }
+    compute_stage_mx(smem + buf * kBufBytes, ad, acc);
+    if (more) store_stage<true>(smem + (buf ^ 1) * kBufBytes, st);
+    lds_barrier();
   }
 }
 
@@ -343,16 +557,12 @@ template <int FA, int FW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(GemmParams p) {
   constexpr bool MX = (FA == MXFP4);
-  using G = Geo<MX>;
-  __shared__ __align__(16) Smem<MX> sm;
+  __shared__ __align__(16) uint8_t smem[kNbuf * kBufBytes];
   int tm, tn;
   tile_coords(p.M, p.N, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-
-  Loader<MX> L;
-  L.init(p, m0, n0);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -360,34 +570,8 @@ void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-  // stages entirely inside K run branch-free; the last stage may be partial
-  const int64_t nfull = p.K / G::BK;
-  const int64_t nstages = (p.K + G::BK - 1) / G::BK;
-  Stage<MX> st;
-  if (nfull > 0) load_full<MX>(L, 0, st);
-  else load_tail<MX>(L, 0, st);
-  store_stage<MX>(sm, 0, st);
-  __syncthreads();
-  auto compute = [&](int buf) {
-    if constexpr (MX) compute_stage_mx(sm, buf, wm, wn, acc);
-    else compute_stage_nv<FA, FW>(sm, buf, wm, wn, p.w_special, acc);
-  };
-  int64_t s = 0;
-  for (; s + 1 < nfull; ++s) {          // next stage is a full one
-    const int buf = (int)(s & 1);
-    load_full<MX>(L, (s + 1) * G::BK, st);
-    compute(buf);
-    store_stage<MX>(sm, buf ^ 1, st);
-    __syncthreads();
-  }
-  for (; s < nstages; ++s) {            // at most two stages: the last full one and the tail
-    const int buf = (int)(s & 1);
-    const bool more = s + 1 < nstages;
-    if (more) load_tail<MX>(L, (s + 1) * G::BK, st);
-    compute(buf);
-    if (more) store_stage<MX>(sm, buf ^ 1, st);
-    __syncthreads();
-  }
+  if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, acc);
+  else mx_tile(p, m0, n0, smem, wm, wn, acc);
 
   const float ga = p.a_global ? *p.a_global : 1.0f;
   const float gw = p.w_global ? *p.w_global : 1.0f;

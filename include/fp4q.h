@@ -153,8 +153,9 @@ fp4q_status fp4q_dequantize(const fp4q_quant_desc* desc, const uint8_t* codes,
  *   a_global, w_global  device FP32 or NULL (= 1.0)
  *   w_special host, 4 floats, required when fw == RAZER_W, else ignored
  *   c         device, M x N (pitch ldc elements), 16-byte aligned
- * Errors: NULL pointer -> ERR_NULL; M, N < 0, K <= 0, K % block, ldc < N
- * -> ERR_SHAPE; a mixed MXFP4/NVFP4 pair or fa == RAZER_W -> ERR_FORMAT;
+ * Errors: NULL pointer -> ERR_NULL; M, N < 0, K <= 0, K % block, K > 2^24
+ * (operand offsets within a 256-row panel are 32-bit), more than 2^31 - 1
+ * tiles of 256 x 256, or ldc < N -> ERR_SHAPE; a mixed MXFP4/NVFP4 pair or fa == RAZER_W -> ERR_FORMAT;
  * bad special value
  * -> ERR_ARG; misalignment -> ERR_ALIGN.  M == 0 or N == 0 enqueues nothing.
  */

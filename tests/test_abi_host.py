@@ -138,7 +138,8 @@ res = {
  "g_mixed": gm(fa=1, fw=0, K=64), "g_razer_w_a": gm(fa=3, fw=3, sp=ctypes.cast(SP, vp)),
  "g_bad_format": gm(fa=4), "g_K_block": gm(K=24), "g_K_mx": gm(fa=1, fw=1, K=48),
  "g_K_zero": gm(K=0), "g_M_neg": gm(M=-1), "g_ldc": gm(ldc=4), "g_align": gm(a=P + 4),
- "g_ldc_align": gm(ldc=9), "g_dtype": gm(ct=3),
+ "g_ldc_align": gm(ldc=9), "g_dtype": gm(ct=3), "g_K_big": gm(K=(1 << 24) + 16),
+ "g_tiles": gm(M=1 << 40, N=1 << 40, ldc=1 << 40),
  "g_bad_special": gm(fw=3, sp=ctypes.cast((ctypes.c_float * 4)(5.0, -5.0, 3.0, -2.5), vp)),
  # channel scale
  "c_null": cs(t=None), "c_rows": cs(rows_x=0), "c_ld": cs(ldx=4), "c_alpha": cs(alpha=float("inf")),
@@ -159,7 +160,7 @@ EXPECTED = {
     "dq_dtype": 5, "dq_format": 4, "dq_block": 5,
     "g_null_a": 1, "g_null_c": 1, "g_null_special": 1, "g_mixed": 4, "g_razer_w_a": 4, "g_bad_format": 4,
     "g_K_block": 2, "g_K_mx": 2, "g_K_zero": 2, "g_M_neg": 2, "g_ldc": 2, "g_align": 3, "g_ldc_align": 3,
-    "g_dtype": 5, "g_bad_special": 5,
+    "g_dtype": 5, "g_bad_special": 5, "g_K_big": 2, "g_tiles": 2,
     "c_null": 1, "c_rows": 2, "c_ld": 2, "c_alpha": 5,
 }
 
