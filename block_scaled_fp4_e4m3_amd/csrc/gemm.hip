@@ -192,27 +192,34 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// a stage entirely inside K with word-aligned scale rows: buffer loads whose
-// only per-stage change is the scalar offset
-template <bool MX>
+// Staging items of a stage: 0..3 the A code chunks, 4..7 the W code chunks,
+// 8 the A scale words, 9 the W scale words.
+constexpr int kItems = 2 * NCH + 2;
+
+// items [I0, I1) of a stage entirely inside K with word-aligned scale rows:
+// buffer loads whose only per-stage change is the scalar offset
+template <bool MX, int I0 = 0, int I1 = kItems>
 __device__ __forceinline__ void load_fast(const Loader<MX>& L, int64_t k0, Stage<MX>& s) {
   const int kb = (int)(k0 / 2), b0 = (int)(k0 / Loader<MX>::BLK);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    s.a[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.ra, (int)L.a_off[i], kb, 0));
-    s.w[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.rw, (int)L.w_off[i], kb, 0));
-  }
-  if constexpr (MX) {
-    s.sa[0] = __builtin_amdgcn_raw_buffer_load_b32(L.rsa, (int)L.sa_off, b0, 0);
-    s.sw[0] = __builtin_amdgcn_raw_buffer_load_b32(L.rsw, (int)L.sw_off, b0, 0);
-  } else {
-    const auto va = __builtin_amdgcn_raw_buffer_load_b64(L.rsa, (int)L.sa_off, b0, 0);
-    const auto vw = __builtin_amdgcn_raw_buffer_load_b64(L.rsw, (int)L.sw_off, b0, 0);
-    s.sa[0] = va[0];
-    s.sa[1] = va[1];
-    s.sw[0] = vw[0];
-    s.sw[1] = vw[1];
-  }
+  static_for<I0, I1>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < NCH) {
+      s.a[i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.ra, (int)L.a_off[i], kb, 0));
+    } else if constexpr (i < 2 * NCH) {
+      s.w[i - NCH] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(L.rw, (int)L.w_off[i - NCH], kb, 0));
+    } else {
+      const __amdgpu_buffer_rsrc_t r = (i == 2 * NCH) ? L.rsa : L.rsw;
+      const int off = (int)((i == 2 * NCH) ? L.sa_off : L.sw_off);
+      uint32_t* dst = (i == 2 * NCH) ? s.sa : s.sw;
+      if constexpr (MX) {
+        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, b0, 0);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, b0, 0);
+        dst[0] = v[0];
+        dst[1] = v[1];
+      }
+    }
+  });
 }
 
 // NS scale bytes of one row from block b0; blocks past the row read as 0
@@ -257,33 +264,30 @@ __device__ __forceinline__ void load_any(const Loader<MX>& L, int64_t k0, Stage<
   scales_bytes<Loader<MX>::NS>(L.sw_row, k0 / Loader<MX>::BLK, L.nblocks, s.sw);
 }
 
-// stage -> LDS buffer at `buf` in fragment order
-template <bool MX>
+// items [I0, I1) of a stage -> LDS buffer at `buf` in fragment order
+template <bool MX, int I0 = 0, int I1 = kItems>
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage<MX>& s) {
   const int t = threadIdx.x;
   uint8_t* ca = buf + code_slot(t / CPR, t % CPR) * 16;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {  // chunk i holds rows 64 i + t / 4: slot + 256 i
-    *(uint4*)(ca + i * 4096) = s.a[i];
-    *(uint4*)(ca + kCodeBytes + i * 4096) = s.w[i];
-  }
-  uint32_t a0, a1, w0, w1;
-  if constexpr (MX) {
-    a0 = __builtin_amdgcn_perm(0u, s.sa[0], 0x0C0C0200u);
-    a1 = __builtin_amdgcn_perm(0u, s.sa[0], 0x0C0C0301u);
-    w0 = __builtin_amdgcn_perm(0u, s.sw[0], 0x0C0C0200u);
-    w1 = __builtin_amdgcn_perm(0u, s.sw[0], 0x0C0C0301u);
-  } else {
-    a0 = __builtin_amdgcn_perm(s.sa[1], s.sa[0], 0x05040100u);
-    a1 = __builtin_amdgcn_perm(s.sa[1], s.sa[0], 0x07060302u);
-    w0 = __builtin_amdgcn_perm(s.sw[1], s.sw[0], 0x05040100u);
-    w1 = __builtin_amdgcn_perm(s.sw[1], s.sw[0], 0x07060302u);
-  }
   uint32_t* sc = (uint32_t*)(buf + 2 * kCodeBytes) + (t >> 5) * 64 + (t & 31);
-  sc[0] = a0;
-  sc[32] = a1;
-  sc[kScaleBytes / 4] = w0;
-  sc[kScaleBytes / 4 + 32] = w1;
+  static_for<I0, I1>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < NCH) {  // chunk i holds rows 64 i + t / 4: slot + 256 i
+      *(uint4*)(ca + i * 4096) = s.a[i];
+    } else if constexpr (i < 2 * NCH) {
+      *(uint4*)(ca + kCodeBytes + (i - NCH) * 4096) = s.w[i - NCH];
+    } else {
+      const uint32_t* src = (i == 2 * NCH) ? s.sa : s.sw;
+      uint32_t* d = sc + ((i == 2 * NCH) ? 0 : kScaleBytes / 4);
+      if constexpr (MX) {
+        d[0] = __builtin_amdgcn_perm(0u, src[0], 0x0C0C0200u);
+        d[32] = __builtin_amdgcn_perm(0u, src[0], 0x0C0C0301u);
+      } else {
+        d[0] = __builtin_amdgcn_perm(src[1], src[0], 0x05040100u);
+        d[32] = __builtin_amdgcn_perm(src[1], src[0], 0x07060302u);
+      }
+    }
+  });
 }
 
 // LDS-only workgroup barrier: waits for this wave's LDS operations, not for
@@ -365,23 +369,56 @@ __device__ __forceinline__ void mfma_step(const half8 (&a)[4], const half8 (&b)[
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
+// Placement of the staging work over the 8 MFMA steps of a stage: step t
+// stores items [store_at[t], store_at[t+1]) of stage s+1 to LDS and issues
+// the global loads of items [load_at[t], load_at[t+1]) of stage s+2 (an item
+// is loaded no earlier than the step that stores its register); chunk-1 codes
+// are read at step read1 (7: stage s+1's, one stage ahead; 1: stage s's).
+struct NvPlan {
+  static constexpr int store_at[9] = {0, 6, 10, 10, 10, 10, 10, 10, 10};
+  static constexpr int load_at[9] = {0, 0, 2, 4, 6, 8, 10, 10, 10};
+  static constexpr int read1 = 7;
+};
+
+template <class P>
+constexpr int plan_ds_writes(int t) {
+  int n = 0;
+  for (int i = P::store_at[t]; i < P::store_at[t + 1]; ++i) n += (i < 2 * NCH) ? 1 : 2;
+  return n;
+}
+
+// every item is reloaded no earlier than the step that stores it, and all
+// stores are issued by the first load step (the generic stage loads all items
+// there)
+template <class P>
+constexpr bool plan_valid() {
+  int first_load = -1;
+  for (int t = 0; t < 8; ++t) {
+    if (first_load < 0 && P::load_at[t] < P::load_at[t + 1]) first_load = t;
+    for (int i = P::load_at[t]; i < P::load_at[t + 1]; ++i)
+      if (!(P::store_at[t + 1] > i)) return false;
+  }
+  return P::store_at[0] == 0 && P::store_at[8] == kItems && P::load_at[0] == 0 && P::load_at[8] == kItems &&
+         first_load >= 0 && P::store_at[first_load + 1] == kItems && (P::read1 == 7 || P::read1 == 1);
+}
+
 // The K loop, software-pipelined across stages.  A stage is 128 elements =
 // 2 chunks x 4 MFMA steps; stage x lives in LDS buffer x % 2.  While the 16
 // MFMAs of step t run, the wave decodes step t + 1 (step 7 decodes the first
 // step of the next stage).  Within stage s:
-//   step 0: store the registers holding stage s+1 into its LDS buffer
-//           (last read during stage s-2, before the barrier of stage s-1);
-//   step 1: issue the global loads of stage s+2 into those registers;
+//   steps per NvPlan: store the registers holding stage s+1 into its LDS
+//           buffer (last read during stage s-1 or s-2, before an earlier
+//           barrier), then reload them with the global loads of stage s+2;
 //   steps 0-1: f16 scale pairs of chunk 1;  end of step 2: LDS barrier;
 //   step 3: read stage s+1's scale dwords and chunk-0 codes;
 //   steps 4-5: f16 scale pairs of stage s+1 chunk 0;
-//   step 7: read stage s+1's chunk-1 codes.
-// Every LDS read is used at least three steps after it is issued and every
-// global load about seven steps after.
-template <int FA, int FW>
+//   step NvPlan::read1: chunk-1 codes.
+// Every LDS read is used at least two steps after it is issued.
+template <int FA, int FW, class P = NvPlan>
 __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
                                         f32x16 (&acc)[4][4]) {
   constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);  // special values need raw scale bytes
+  static_assert(plan_valid<P>(), "staging plan");
   Loader<false> L;
   L.init(p, m0, n0);
   const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
@@ -409,7 +446,7 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
   NvRegs R;
   read_scales(smem, ad, R.ra, R.rw);
   read_codes(smem, ad, 0, R.ca0, R.cw0);
-  read_codes(smem, ad, 1, R.ca1, R.cw1);
+  if constexpr (P::read1 == 7) read_codes(smem, ad, 1, R.ca1, R.cw1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
@@ -423,16 +460,18 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
   // reads of the next stage read a stale buffer, which is harmless.
   auto stage = [&](int64_t s, auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
-    const uint8_t* rbuf = smem + ((s + 1) & 1) * kBufBytes;
-    uint8_t* wbuf = smem + ((s + 1) & 1) * kBufBytes;
+    uint8_t* nbuf = smem + ((s + 1) & 1) * kBufBytes;   // stage s+1
+    const uint8_t* cbuf = smem + (s & 1) * kBufBytes;   // stage s
     static_for<0, 8>([&](auto tc) {
       constexpr int t = decltype(tc)::value, cur = t & 1;
-      if constexpr (t == 0) {
-        if (FAST || s + 1 < nstages) store_stage<false>(wbuf, st);
+      constexpr int st0 = P::store_at[t], st1 = P::store_at[t + 1];
+      constexpr int ld0 = P::load_at[t], ld1 = P::load_at[t + 1];
+      if constexpr (st0 < st1) {
+        if (FAST || s + 1 < nstages) store_stage<false, st0, st1>(nbuf, st);
       }
-      if constexpr (t == 1) {
-        if constexpr (FAST) load_fast<false>(L, (s + 2) * BK, st);
-        else if (s + 2 < nstages) gload(s + 2);
+      if constexpr (ld0 < ld1) {
+        if constexpr (FAST) load_fast<false, ld0, ld1>(L, (s + 2) * BK, st);
+        else if (ld0 == 0 && s + 2 < nstages) gload(s + 2);
       }
       if constexpr (t == 0 || t == 1) {  // chunk-1 scale pairs, A at step 0, W at step 1
 #pragma unroll
@@ -446,9 +485,13 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
           }
         }
       }
+      if constexpr (t == P::read1) {
+        if constexpr (t == 7) read_codes(nbuf, ad, 1, R.ca1, R.cw1);
+        else read_codes(cbuf, ad, 1, R.ca1, R.cw1);
+      }
       if constexpr (t == 3) {
-        read_scales(rbuf, ad, R.ra, R.rw);
-        read_codes(rbuf, ad, 0, R.ca0, R.cw0);
+        read_scales(nbuf, ad, R.ra, R.rw);
+        read_codes(nbuf, ad, 0, R.ca0, R.cw0);
       }
       if constexpr (t == 4 || t == 5) {  // next stage's chunk-0 scale pairs
 #pragma unroll
@@ -457,7 +500,6 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
           else R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
         }
       }
-      if constexpr (t == 7) read_codes(rbuf, ad, 1, R.ca1, R.cw1);
       // decode of step t + 1
       if constexpr (t < 3)
         decode_step<FA, FW, 0, t + 1>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
@@ -467,12 +509,9 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
         decode_step<FA, FW, 0, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
       mfma_step(da[cur], db[cur], acc);
       if constexpr (FAST) {
-        if constexpr (t == 0) sched_step<2 * NCH + 4, 0, 0, 5>();
-        else if constexpr (t == 1) sched_step<0, 2 * NCH + 2, 0, 5>();
-        else if constexpr (t == 3) sched_step<0, 0, 16, 4>();
-        else if constexpr (t == 4 || t == 5) sched_step<0, 0, 0, 5>();
-        else if constexpr (t == 7) sched_step<0, 0, 8, 4>();
-        else sched_step<0, 0, 0, 4>();
+        constexpr int ndsr = (t == 3 ? 16 : 0) + (t == P::read1 ? 8 : 0);
+        constexpr int extra = (t == 0 || t == 1 || t == 4 || t == 5) || plan_ds_writes<P>(t) > 8 ? 5 : 4;
+        sched_step<plan_ds_writes<P>(t), ld1 - ld0, ndsr, extra>();
       }
       if constexpr (t == 2) lds_barrier();
     });
@@ -484,27 +523,43 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
 }
 
 // ---------------------------------------------------------------- MXFP4 K loop
-// 2 chunks of 64 per stage, 16 block-scaled MFMAs per chunk; the MFMA takes
-// the stage scale dword and selects the chunk's byte.
-__device__ __forceinline__ void compute_stage_mx(const uint8_t* buf, const NvAddr& ad, f32x16 (&acc)[4][4]) {
-  uint32_t sa[4], sw[4];
-  read_scales(buf, ad, sa, sw);
-  static_for<0, 2>([&](auto kcc) {
-    constexpr int kc = decltype(kcc)::value;
-    uint4 ca[4], cw[4];
-    read_codes(buf, ad, kc, ca, cw);
+// 8 block-scaled MFMAs: chunk KC, A tiles I0 and I0 + 1 x the 4 W tiles; the
+// MFMA takes the stage scale dword and selects the chunk's byte
+template <int KC, int I0>
+__device__ __forceinline__ void mx_mfma_half(const uint4 (&ca)[4], const uint4 (&cw)[4], const uint32_t (&sa)[4],
+                                             const uint32_t (&sw)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = I0; i < I0 + 2; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const i32x8 a = {(int)ca[i].x, (int)ca[i].y, (int)ca[i].z, (int)ca[i].w, 0, 0, 0, 0};
-        const i32x8 b = {(int)cw[jj].x, (int)cw[jj].y, (int)cw[jj].z, (int)cw[jj].w, 0, 0, 0, 0};
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][jj], 4, 4, kc, (int)sa[i], kc,
-                                                                      (int)sw[jj]);
-      }
-  });
+    for (int j = 0; j < 4; ++j) {
+      const i32x8 a = {(int)ca[i].x, (int)ca[i].y, (int)ca[i].z, (int)ca[i].w, 0, 0, 0, 0};
+      const i32x8 b = {(int)cw[j].x, (int)cw[j].y, (int)cw[j].z, (int)cw[j].w, 0, 0, 0, 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, KC, (int)sa[i], KC, (int)sw[j]);
+    }
 }
 
+template <int NDSW, int NVMEM, int NDSR>
+__device__ __forceinline__ void sched_mx_step() {
+  static_for<0, 8>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (k < NDSW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if constexpr (k < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if constexpr (k < NDSR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The MXFP4 K loop, pipelined across stages like the NVFP4 one.  A stage is
+// 2 chunks = 4 steps of 8 MFMAs; stage x lives in LDS buffer x % 2.  Within
+// stage s:
+//   step 0: read stage s's chunk-1 codes; store the first items of stage s+1;
+//   step 1: store the rest; issue the first global loads of stage s+2; end
+//           of step 1: LDS barrier;
+//   step 2: keep stage s's scale dwords for chunk 1, read stage s+1's scale
+//           dwords and chunk-0 codes; issue the remaining global loads.
+// Chunk-0 codes are read two steps before use, chunk-1 codes likewise.
 __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
                                         f32x16 (&acc)[4][4]) {
   Loader<true> L;
@@ -520,35 +575,56 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
   }
   ad.sa = 2 * kCodeBytes + (wm * 4 * 64 + lane) * 4;
   ad.sw = 2 * kCodeBytes + kScaleBytes + (wn * 4 * 64 + lane) * 4;
-  // stages entirely inside K run branch-free; the last stage may be partial
-  const int64_t nfull = p.K / BK;
-  const int64_t nstages = (p.K + BK - 1) / BK;
+  const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
   Stage<true> st;
-  if (nfull > 0 && L.vec_scales) load_fast<true>(L, 0, st);
-  else load_any<true>(L, 0, st);
+  auto gload = [&](int64_t stg) {
+    if (stg < nfull && L.vec_scales) load_fast<true>(L, stg * BK, st);
+    else load_any<true>(L, stg * BK, st);
+  };
+  gload(0);
   store_stage<true>(smem, st);
+  if (nstages > 1) gload(1);
   lds_barrier();
-  int64_t s = 0;
-  if (L.vec_scales) {
-    for (; s + 1 < nfull; ++s) {          // next stage is a full one
-      const int buf = (int)(s & 1);
-      load_fast<true>(L, (s + 1) * BK, st);
-      compute_stage_mx(smem + buf * kBufBytes, ad, acc);
-      store_stage<true>(smem + (buf ^ 1) * kBufBytes, st);
-      lds_barrier();
-    }
-  }
-  for (; s < nstages; ++s) {
-    const int buf = (int)(s & 1);
-    const bool more = s + 1 < nstages;
-    if (more) {
-      if (s + 1 < nfull && L.vec_scales) load_fast<true>(L, (s + 1) * BK, st);
-      else load_any<true>(L, (s + 1) * BK, st);
-    }
-    compute_stage_mx(smem + buf * kBufBytes, ad, acc);
-    if (more) store_stage<true>(smem + (buf ^ 1) * kBufBytes, st);
+  uint4 ca0[4], cw0[4], ca1[4], cw1[4];
+  uint32_t sa[4], sw[4], qa[4], qw[4];
+  read_scales(smem, ad, sa, sw);
+  read_codes(smem, ad, 0, ca0, cw0);
+
+  auto stage = [&](int64_t s, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    uint8_t* nbuf = smem + ((s + 1) & 1) * kBufBytes;   // stage s+1
+    const uint8_t* cbuf = smem + (s & 1) * kBufBytes;   // stage s
+    // step 0
+    read_codes(cbuf, ad, 1, ca1, cw1);
+    if (FAST || s + 1 < nstages) store_stage<true, 0, 6>(nbuf, st);
+    mx_mfma_half<0, 0>(ca0, cw0, sa, sw, acc);
+    if constexpr (FAST) sched_mx_step<6, 0, 4>();
+    // step 1
+    if (FAST || s + 1 < nstages) store_stage<true, 6, kItems>(nbuf, st);
+    if constexpr (FAST) load_fast<true, 0, 5>(L, (s + 2) * BK, st);
+    else if (s + 2 < nstages) gload(s + 2);
+    mx_mfma_half<0, 2>(ca0, cw0, sa, sw, acc);
+    if constexpr (FAST) sched_mx_step<6, 5, 0>();
     lds_barrier();
-  }
+    // step 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qa[i] = sa[i];
+      qw[i] = sw[i];
+    }
+    read_scales(nbuf, ad, sa, sw);
+    read_codes(nbuf, ad, 0, ca0, cw0);
+    if constexpr (FAST) load_fast<true, 5, kItems>(L, (s + 2) * BK, st);
+    mx_mfma_half<1, 0>(ca1, cw1, qa, qw, acc);
+    if constexpr (FAST) sched_mx_step<0, 5, 8>();
+    // step 3
+    mx_mfma_half<1, 2>(ca1, cw1, qa, qw, acc);
+    if constexpr (FAST) sched_mx_step<0, 0, 0>();
+  };
+  int64_t s = 0;
+  if (L.vec_scales)
+    for (; s + 2 < nfull; ++s) stage(s, std::true_type{});
+  for (; s < nstages; ++s) stage(s, std::false_type{});
 }
 
 // ---------------------------------------------------------------- kernel
