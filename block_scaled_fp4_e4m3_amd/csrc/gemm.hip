@@ -551,15 +551,24 @@ __device__ __forceinline__ void sched_mx_step() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// global loads of stage s+3 in MXFP4 stage s: items [0, load_at[1]) at step 1,
+// [load_at[1], load_at[2]) at step 2, the rest at step 3
+struct MxPlan {
+  static constexpr int load_at[3] = {0, 5, 10};
+};
+
 // The MXFP4 K loop, pipelined across stages like the NVFP4 one.  A stage is
-// 2 chunks = 4 steps of 8 MFMAs; stage x lives in LDS buffer x % 2.  Within
-// stage s:
+// 2 chunks = 4 steps of 8 MFMAs (a quarter of an NVFP4 stage's time), so the
+// global loads run further ahead: two register staging sets alternate by
+// stage parity, and stage s stores set s % 2 (stage s+1, loaded during stage
+// s-2) and then reloads it with stage s+3.  Stage x lives in LDS buffer x % 2.
+// Within stage s:
 //   step 0: read stage s's chunk-1 codes; store the first items of stage s+1;
-//   step 1: store the rest; issue the first global loads of stage s+2; end
+//   step 1: store the rest; issue the first global loads of stage s+3; end
 //           of step 1: LDS barrier;
 //   step 2: keep stage s's scale dwords for chunk 1, read stage s+1's scale
 //           dwords and chunk-0 codes; issue the remaining global loads.
-// Chunk-0 codes are read two steps before use, chunk-1 codes likewise.
+// Chunk-0 and chunk-1 codes are read two steps before use.
 __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
                                         f32x16 (&acc)[4][4]) {
   Loader<true> L;
@@ -576,35 +585,38 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
   ad.sa = 2 * kCodeBytes + (wm * 4 * 64 + lane) * 4;
   ad.sw = 2 * kCodeBytes + kScaleBytes + (wn * 4 * 64 + lane) * 4;
   const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
-  Stage<true> st;
-  auto gload = [&](int64_t stg) {
-    if (stg < nfull && L.vec_scales) load_fast<true>(L, stg * BK, st);
-    else load_any<true>(L, stg * BK, st);
+  Stage<true> st[2];
+  auto gload = [&](int64_t stg, Stage<true>& dst) {
+    if (stg < nfull && L.vec_scales) load_fast<true>(L, stg * BK, dst);
+    else load_any<true>(L, stg * BK, dst);
   };
-  gload(0);
-  store_stage<true>(smem, st);
-  if (nstages > 1) gload(1);
+  gload(0, st[0]);
+  store_stage<true>(smem, st[0]);
+  if (nstages > 1) gload(1, st[0]);
+  if (nstages > 2) gload(2, st[1]);
   lds_barrier();
   uint4 ca0[4], cw0[4], ca1[4], cw1[4];
   uint32_t sa[4], sw[4], qa[4], qw[4];
   read_scales(smem, ad, sa, sw);
   read_codes(smem, ad, 0, ca0, cw0);
 
-  auto stage = [&](int64_t s, auto fast_tag) {
+  auto stage = [&](int64_t s, auto fast_tag, auto par_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    Stage<true>& sg = st[PAR];
     uint8_t* nbuf = smem + ((s + 1) & 1) * kBufBytes;   // stage s+1
     const uint8_t* cbuf = smem + (s & 1) * kBufBytes;   // stage s
     // step 0
     read_codes(cbuf, ad, 1, ca1, cw1);
-    if (FAST || s + 1 < nstages) store_stage<true, 0, 6>(nbuf, st);
+    if (FAST || s + 1 < nstages) store_stage<true, 0, 6>(nbuf, sg);
     mx_mfma_half<0, 0>(ca0, cw0, sa, sw, acc);
     if constexpr (FAST) sched_mx_step<6, 0, 4>();
     // step 1
-    if (FAST || s + 1 < nstages) store_stage<true, 6, kItems>(nbuf, st);
-    if constexpr (FAST) load_fast<true, 0, 5>(L, (s + 2) * BK, st);
-    else if (s + 2 < nstages) gload(s + 2);
+    if (FAST || s + 1 < nstages) store_stage<true, 6, kItems>(nbuf, sg);
+    if constexpr (FAST) load_fast<true, 0, MxPlan::load_at[1]>(L, (s + 3) * BK, sg);
+    else if (s + 3 < nstages) gload(s + 3, sg);
     mx_mfma_half<0, 2>(ca0, cw0, sa, sw, acc);
-    if constexpr (FAST) sched_mx_step<6, 5, 0>();
+    if constexpr (FAST) sched_mx_step<6, MxPlan::load_at[1], 0>();
     lds_barrier();
     // step 2
 #pragma unroll
@@ -614,17 +626,26 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
     }
     read_scales(nbuf, ad, sa, sw);
     read_codes(nbuf, ad, 0, ca0, cw0);
-    if constexpr (FAST) load_fast<true, 5, kItems>(L, (s + 2) * BK, st);
+    if constexpr (FAST) load_fast<true, MxPlan::load_at[1], MxPlan::load_at[2]>(L, (s + 3) * BK, sg);
     mx_mfma_half<1, 0>(ca1, cw1, qa, qw, acc);
-    if constexpr (FAST) sched_mx_step<0, 5, 8>();
+    if constexpr (FAST) sched_mx_step<0, MxPlan::load_at[2] - MxPlan::load_at[1], 8>();
     // step 3
+    if constexpr (FAST) load_fast<true, MxPlan::load_at[2], kItems>(L, (s + 3) * BK, sg);
     mx_mfma_half<1, 2>(ca1, cw1, qa, qw, acc);
-    if constexpr (FAST) sched_mx_step<0, 0, 0>();
+    if constexpr (FAST) sched_mx_step<0, kItems - MxPlan::load_at[2], 0>();
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   int64_t s = 0;
   if (L.vec_scales)
-    for (; s + 2 < nfull; ++s) stage(s, std::true_type{});
-  for (; s < nstages; ++s) stage(s, std::false_type{});
+    for (; s + 4 < nfull; s += 2) {   // stages s, s+1 load stages s+3, s+4
+      stage(s, std::true_type{}, P0{});
+      stage(s + 1, std::true_type{}, P1{});
+    }
+  for (; s < nstages; s += 2) {       // s is even here
+    stage(s, std::false_type{}, P0{});
+    if (s + 1 < nstages) stage(s + 1, std::false_type{}, P1{});
+  }
 }
 
 // ---------------------------------------------------------------- kernel

@@ -34,6 +34,20 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
 
+// value of lane ^ D within a quad (D = 1, 2) through a DPP quad permutation;
+// other distances through the LDS crossbar
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  else if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  else return (uint32_t)__shfl_xor((int)v, D);
+}
+__device__ __forceinline__ float lane_xor_f(float v, int d) {
+  if (d == 1) return bitsf(lane_xor<1>(fbits(v)));
+  if (d == 2) return bitsf(lane_xor<2>(fbits(v)));
+  return __shfl_xor(v, d);
+}
+
 // strict-greater threshold bits for "round up past T" decisions:
 // tie_up = false:  |x| > T  <=>  bits(|x|) > bits(RD32(T))
 // tie_up = true :  |x| >= T <=>  bits(|x|) > bits(RU32(T)) - 1
@@ -186,31 +200,48 @@ __device__ __forceinline__ float tree_sum(const float* p) {
   else return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// load L elements of row r starting at column j0, apply the channel scale and
-// the size-32 block-Hadamard (lanes of a 32-group are adjacent)
+// the raw input words of one chunk (L bf16 or L fp32 values)
 template <int L, bool BF16>
-__device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int64_t j0, float* x,
-                                           bool chan, bool had) {
+struct Raw {
+  static constexpr int W = BF16 ? L / 2 : L;  // 32-bit words
+  uint32_t w[W];
+};
+
+template <int L, bool BF16>
+__device__ __forceinline__ void load_raw(const QuantParams& p, int64_t r, int64_t j0, Raw<L, BF16>& raw) {
   if constexpr (BF16) {
     const uint16_t* src = (const uint16_t*)p.x + r * p.ld + j0;
     if constexpr (L == 8) {
-      uint4 v = *(const uint4*)src;
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
+      const uint4 v = *(const uint4*)src;
+      raw.w[0] = v.x; raw.w[1] = v.y; raw.w[2] = v.z; raw.w[3] = v.w;
     } else {
-      uint2 v = *(const uint2*)src;
-      uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-      for (int i = 0; i < 2; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
+      const uint2 v = *(const uint2*)src;
+      raw.w[0] = v.x; raw.w[1] = v.y;
     }
   } else {
     const float* src = (const float*)p.x + r * p.ld + j0;
 #pragma unroll
     for (int i = 0; i < L; i += 4) {
-      float4 v = *(const float4*)(src + i);
-      x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+      const uint4 v = *(const uint4*)(src + i);
+      raw.w[i] = v.x; raw.w[i + 1] = v.y; raw.w[i + 2] = v.z; raw.w[i + 3] = v.w;
     }
+  }
+}
+
+// widen a raw chunk, apply the channel scale and the size-32 block-Hadamard
+// (lanes of a 32-group are adjacent)
+template <int L, bool BF16>
+__device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, const Raw<L, BF16>& raw, float* x,
+                                             bool chan, bool had) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < L / 2; ++i) {
+      x[2 * i] = bitsf(raw.w[i] << 16);
+      x[2 * i + 1] = bitsf(raw.w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) x[i] = bitsf(raw.w[i]);
   }
   if (chan) {
 #pragma unroll
@@ -239,7 +270,7 @@ __device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int6
       const bool lower = (lane & d) == 0;
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        float o = __shfl_xor(x[i], d);
+        float o = lane_xor_f(x[i], d);
         x[i] = lower ? (x[i] + o) : (o - x[i]);
       }
     }
@@ -247,6 +278,14 @@ __device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int6
 #pragma unroll
     for (int i = 0; i < L; ++i) x[i] = x[i] * c;
   }
+}
+
+template <int L, bool BF16>
+__device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int64_t j0, float* x,
+                                           bool chan, bool had) {
+  Raw<L, BF16> raw;
+  load_raw<L, BF16>(p, r, j0, raw);
+  finish_chunk<L, BF16>(p, j0, raw, x, chan, had);
 }
 
 // encode L elements with thresholds t; returns packed nibbles
@@ -281,6 +320,67 @@ __device__ __forceinline__ uint32_t encode_special(const float* x, const uint32_
   return packed;
 }
 
+// E4M3 scale code (0..126) -> its value as FP32: the hardware FP8 decode
+// (OCP E4M3, exact) with unit scale
+__device__ __forceinline__ float e4m3_f32(int k) { return __builtin_amdgcn_cvt_scalef32_f32_fp8(k, 1.0f, 0); }
+
+// codes whose magnitude rounded to 0 carry the sign of x in the hardware
+// convert (code 0x8); the format writes them as 0
+__device__ __forceinline__ uint32_t clear_neg_zero(uint32_t packed) {
+  const uint32_t nz = ((packed & 0x77777777u) + 0x77777777u) & 0x88888888u;  // bit 3: magnitude != 0
+  return packed & ~(packed & 0x88888888u & ~nz);
+}
+
+// Bracketed hardware encode.  The gfx950 FP4 convert rounds to nearest even
+// (saturating) after dividing by the power-of-two part of its scale, which is
+// 1 here.  Each element is converted at x * rlo and x * rhi, where
+// rlo < 1/(s g) < rhi with a relative margin far above the rounding errors of
+// forming them and of the product, so the exact ratio |x| / (s g) lies
+// strictly between the two converted values.  Rounding is monotone: equal
+// codes at both ends are the exact decision.  `ok` is false when some element
+// may sit on or near a rounding midpoint; that block then takes the threshold
+// path.
+template <int L>
+__device__ __forceinline__ uint32_t encode_bracket(const float* x, float rlo, float rhi, bool& ok) {
+  uint32_t plo = 0, phi = 0;
+  static_for<0, L / 2>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    plo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(plo, x[2 * b] * rlo, x[2 * b + 1] * rlo, 1.0f, b);
+    phi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(phi, x[2 * b] * rhi, x[2 * b + 1] * rhi, 1.0f, b);
+  });
+  ok = plo == phi;
+  return clear_neg_zero(plo);
+}
+
+template <int LPB>
+__device__ __forceinline__ bool group_all(bool v) {
+  uint32_t b = v ? 1u : 0u;
+  if constexpr (LPB >= 2) b &= lane_xor<1>(b);
+  if constexpr (LPB >= 4) b &= lane_xor<2>(b);
+  return b != 0;
+}
+
+// NVFP4 codes of a lane's L elements for scale code k (value s) under global
+// g: bracketed convert, threshold path for blocks it cannot decide.  The
+// bracket is used only for finite blocks with s g well inside the normal range.
+template <int L, int LPB, int FMT>
+__device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, float g, bool finite,
+                                              const Tables<FMT>& T) {
+  const float sg = s * g;
+  const float r = __builtin_amdgcn_rcpf(sg);  // within 1 ulp of 1 / RN(s g)
+  bool ok = finite && sg > 0x1p-120f && sg < 0x1p120f;
+  const float rlo = r * (1.0f - 0x1p-20f), rhi = r * (1.0f + 0x1p-20f);
+  bool same;
+  uint32_t packed = encode_bracket<L>(x, rlo, rhi, same);
+  if (!group_all<LPB>(ok && same)) {
+    uint32_t t[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
+    packed = encode_plain<L>(x, t);
+  }
+  return packed;
+}
+
 // block error of a lane's L elements (lane part of the balanced tree);
 // value of a code via the hardware FP4 -> FP32 convert (scale 1.0 is exact)
 template <int L>
@@ -305,18 +405,21 @@ __device__ __forceinline__ float lane_sse(const float* x, uint32_t packed, float
 
 template <int LPB>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < LPB; d *= 2) v = v + __shfl_xor(v, d);
+  if constexpr (LPB >= 2) v = v + bitsf(lane_xor<1>(fbits(v)));
+  if constexpr (LPB >= 4) v = v + bitsf(lane_xor<2>(fbits(v)));
+  static_assert(LPB <= 4, "blocks span at most 4 lanes");
   return v;
 }
 template <int LPB>
 __device__ __forceinline__ uint32_t group_max(uint32_t v) {
-#pragma unroll
-  for (int d = 1; d < LPB; d *= 2) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+  if constexpr (LPB >= 2) v = max(v, lane_xor<1>(v));
+  if constexpr (LPB >= 4) v = max(v, lane_xor<2>(v));
   return v;
 }
 
-template <int FMT, int B, int RULE, bool BF16>
+// CONTIG: rows are contiguous (ld == cols) and there is no channel scale, so
+// the tensor is walked as one row of rows * cols elements
+template <int FMT, int B, int RULE, bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   constexpr int L = (B == 4) ? 4 : 8;
   constexpr int LPB = B / L;  // lanes per block
@@ -334,14 +437,52 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const double inv4 = 1.0 / (4.0 * (double)g);
   constexpr int SF = FmtTraits<FMT>::SF;
 
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c - threadIdx.x < total; c += stride) {
+  // E4M3 scale selection by the hardware FP32 -> E4M3 convert (nearest even;
+  // above 464 it gives the NaN code, which stands for the saturated 126):
+  // amax / (6 g) and amax / (4 g) are bracketed like the element ratios in
+  // encode_nv, and equal codes at both ends are the exact choice
+  const bool fast_scale = g > 0x1p-100f && g < 0x1p100f;
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * g), r4 = __builtin_amdgcn_rcpf(4.0f * g);
+  const float lo6 = r6 * (1.0f - 0x1p-20f), hi6 = r6 * (1.0f + 0x1p-20f);
+  const float lo4 = r4 * (1.0f - 0x1p-20f), hi4 = r4 * (1.0f + 0x1p-20f);
+
+  // chunk c = r * cpr + cj; the division happens once, then (r, cj) advance.
+  // Each iteration issues the loads of U chunks (c, c + stride, ...) before
+  // working on the first, to keep enough bytes in flight per CU.
+  constexpr int U = 4;
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t r0 = CONTIG ? 0 : c / cpr, cj0 = CONTIG ? c : c % cpr;
+  const int64_t sr = CONTIG ? 0 : stride / cpr, sc = CONTIG ? stride : stride % cpr;
+  for (; c - threadIdx.x < total; c += U * stride) {
     // whole waves stay in the loop so that shuffles see their partners; lanes
     // past the end work on a clamped chunk and store nothing
-    const bool valid = c < total;
-    const int64_t cc = valid ? c : total - 1;
-    const int64_t r = cc / cpr, cj = cc % cpr;
+    Raw<L, BF16> raw[U];
+    int64_t ru[U], cu[U];
+    bool vu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      vu[u] = c + u * stride < total;
+      if constexpr (CONTIG) {
+        ru[u] = 0;
+        cu[u] = vu[u] ? c + u * stride : total - 1;
+      } else {
+        ru[u] = vu[u] ? r0 : p.rows - 1;
+        cu[u] = vu[u] ? cj0 : cpr - 1;
+        r0 += sr;
+        cj0 += sc;
+        if (cj0 >= cpr) {
+          cj0 -= cpr;
+          ++r0;
+        }
+      }
+      load_raw<L, BF16>(p, ru[u], cu[u] * L, raw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+    const bool valid = vu[u];
+    const int64_t r = ru[u], cj = cu[u];
     float x[L];
-    load_chunk<L, BF16>(p, r, cj * L, x, chan, had);
+    finish_chunk<L, BF16>(p, cj * L, raw[u], x, chan, had);
 
     uint32_t amax = 0;
 #pragma unroll
@@ -359,13 +500,25 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         int fl = ex ? ex - 127 : (31 - __clz((int)amax)) - 149;
         E = max(-127, fl - 2);
       }
-      uint32_t t[7];
+      // the convert divides by 2^E exactly (E >= -126: a normal FP32 scale)
+      // and rounds to nearest even, which is the format's rounding
+      if (E >= -126 && amax < 0x7F800000u) {
+        packed = 0;
+        const float sc = bitsf((uint32_t)(E + 127) << 23);
+        static_for<0, L / 2>([&](auto ic) {
+          constexpr int b = decltype(ic)::value;
+          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, x[2 * b], x[2 * b + 1], sc, b);
+        });
+        packed = clear_neg_zero(packed);
+      } else {
+        uint32_t t[7];
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        uint32_t b = fbits(ldexpf(kMid[j], E));   // exact
-        t[j] = (j & 1) ? b - 1 : b;
+        for (int j = 0; j < 7; ++j) {
+          uint32_t b = fbits(ldexpf(kMid[j], E));   // exact
+          t[j] = (j & 1) ? b - 1 : b;
+        }
+        packed = encode_plain<L>(x, t);
       }
-      packed = encode_plain<L>(x, t);
       sbyte = (uint8_t)(E + 127);
     } else if constexpr (FMT == NVFP4) {
       if constexpr (RULE == BRUTE) {
@@ -383,21 +536,34 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         }
         sbyte = (uint8_t)bestk;
       } else {
-        int k6 = select_scale<0>(bitsf(amax), T.smid6, inv6);
+        const bool finite = amax < 0x7F800000u;
+        int k6 = 0, k4 = 0;
+        bool sok = false;
+        if (fast_scale && finite) {
+          typedef short s2v __attribute__((ext_vector_type(2)));
+          const float a = bitsf(amax);
+          const s2v z = {0, 0};
+          const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * lo6, a * lo4, 1.0f, false);
+          const s2v chi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * hi6, a * hi4, 1.0f, false);
+          const uint32_t wl = (uint16_t)clo[0], wh = (uint16_t)chi[0];
+          k6 = min((int)(wl & 0xFFu), 126);
+          k4 = min((int)(wl >> 8), 126);
+          sok = k6 == min((int)(wh & 0xFFu), 126) && (RULE != FOUR6 || k4 == min((int)(wh >> 8), 126));
+        }
+        if (!sok) {
+          k6 = select_scale<0>(bitsf(amax), T.smid6, inv6);
+          if constexpr (RULE == FOUR6) k4 = select_scale<0>(bitsf(amax), T.smid4, inv4);
+        }
         if (p.prevent_zero && k6 == 0) k6 = 1;
-        uint32_t t[7];
-#pragma unroll
-        for (int j = 0; j < 7; ++j) t[j] = T.elt[k6][j];
-        packed = encode_plain<L>(x, t);
+        const float s6 = e4m3_f32(k6);
+        packed = encode_nv<L, LPB>(x, k6, s6, g, finite, T);
         sbyte = (uint8_t)k6;
         if constexpr (RULE == FOUR6) {
-          int k4 = select_scale<0>(bitsf(amax), T.smid4, inv4);
           if (p.prevent_zero && k4 == 0) k4 = 1;
-#pragma unroll
-          for (int j = 0; j < 7; ++j) t[j] = T.elt[k4][j];
-          uint32_t pk4 = encode_plain<L>(x, t);
-          float e6 = group_sum<LPB>(lane_sse<L>(x, packed, (float)sf_val<0>(k6), g, false, 0.f));
-          float e4 = group_sum<LPB>(lane_sse<L>(x, pk4, (float)sf_val<0>(k4), g, false, 0.f));
+          const float s4 = e4m3_f32(k4);
+          uint32_t pk4 = encode_nv<L, LPB>(x, k4, s4, g, finite, T);
+          float e6 = group_sum<LPB>(lane_sse<L>(x, packed, s6, g, false, 0.f));
+          float e4 = group_sum<LPB>(lane_sse<L>(x, pk4, s4, g, false, 0.f));
           if (e4 < e6) { packed = pk4; sbyte = (uint8_t)k4; }
         }
       }
@@ -430,16 +596,32 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     }
 
     if (valid) {
-      uint8_t* dst = p.codes + r * (p.cols / 2) + cj * (L / 2);
+      uint8_t* dst = p.codes + (CONTIG ? 0 : r * (p.cols / 2)) + cj * (L / 2);
       if constexpr (L == 8) *(uint32_t*)dst = packed;
       else *(uint16_t*)dst = (uint16_t)packed;
-      if (cj % LPB == 0) p.scales[r * (p.cols / B) + cj / LPB] = sbyte;
+      if (cj % LPB == 0) p.scales[(CONTIG ? 0 : r * (p.cols / B)) + cj / LPB] = sbyte;
     }
+    }  // u
   }
 }
 
 // ---------------------------------------------------------------- global amax
 __global__ void zero_global_kernel(float* g) { *(uint32_t*)g = 0u; }
+
+// workgroup maximum, then one atomic per workgroup
+__device__ __forceinline__ void block_max_to_global(uint32_t m, unsigned int* dst) {
+  __shared__ uint32_t part[kThreads / 64];
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = part[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) v = max(v, part[w]);
+    atomicMax(dst, v);
+  }
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(QuantParams p) {
@@ -459,9 +641,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(QuantParams p) {
 #pragma unroll
       for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
   }
-#pragma unroll
-  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.global, m);
+  block_max_to_global(m, (unsigned int*)p.global);
 }
 
 template <bool BF16>
@@ -479,9 +659,7 @@ __global__ __launch_bounds__(kThreads) void amax4_kernel(QuantParams p) {
 #pragma unroll
     for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
   }
-#pragma unroll
-  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.global, m);
+  block_max_to_global(m, (unsigned int*)p.global);
 }
 
 // "Finer is Better" Method 2 hierarchical scaling: g maps the tensor maximum
@@ -572,9 +750,8 @@ __global__ __launch_bounds__(kThreads) void channel_scale_kernel(ChanScaleParams
   }
 }
 
-int grid_for(int64_t work_items) {
+int grid_for(int64_t work_items, int64_t cap = 256 * 16) {  // default: 16 workgroups per CU on 256 CUs
   int64_t blocks = (work_items + kThreads - 1) / kThreads;
-  const int64_t cap = 256 * 16;  // 16 workgroups per CU on 256 CUs
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return (int)blocks;
@@ -584,8 +761,15 @@ template <int FMT, int B, int RULE>
 hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   constexpr int L = (B == 4) ? 4 : 8;
   int grid = grid_for(p.rows * (p.cols / L));
-  if (bf16) hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, true>), dim3(grid), dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  // the brute-force search is compute-bound: one addressing variant suffices
+  const bool contig = RULE != BRUTE && p.ld == p.cols && p.chan_scale == nullptr;
+  if (contig) {
+    if (bf16) hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, true, RULE != BRUTE>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, false, RULE != BRUTE>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else {
+    if (bf16) hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, true, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, false, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -608,11 +792,11 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
   if (gmode == G_AUTO) {
     hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
     if (p.cols % 8 == 0) {
-      int grid = grid_for(p.rows * (p.cols / 8));
+      int grid = grid_for(p.rows * (p.cols / 8), 256 * 4);
       if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
     } else {
-      int grid = grid_for(p.rows * (p.cols / 4));
+      int grid = grid_for(p.rows * (p.cols / 4), 256 * 4);
       if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL(amax4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
     }
