@@ -79,6 +79,7 @@ __device__ __forceinline__ double sf_val(int k) {
 
 // E2M1 magnitudes and the midpoints between neighbours
 __constant__ float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+constexpr double kMidD[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
 __constant__ float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
 
 template <int FMT> struct FmtTraits;
@@ -150,9 +151,9 @@ __device__ void build_tables(Tables<FMT>& T, float g, const float* special) {
   }
 }
 
-// nearest scale code to a/(T g) from the midpoint table; guess in binary64
+// scale code guess for a/(T g) in binary64, off by at most one
 template <int SF>
-__device__ __forceinline__ int select_scale(float a, const uint32_t* smid, double inv_Tg) {
+__device__ __forceinline__ int select_scale_guess(float a, double inv_Tg) {
   constexpr int KMAX = SF == 0 ? 126 : 63;
   double y = (double)a * inv_Tg;
   int k;
@@ -173,6 +174,14 @@ __device__ __forceinline__ int select_scale(float a, const uint32_t* smid, doubl
       k = ((e + 3) << 3) | (int)((b >> 49) & 7);
     }
   }
+  return k;
+}
+
+// nearest scale code to a/(T g) from the midpoint table
+template <int SF>
+__device__ __forceinline__ int select_scale(float a, const uint32_t* smid, double inv_Tg) {
+  constexpr int KMAX = SF == 0 ? 126 : 63;
+  int k = select_scale_guess<SF>(a, inv_Tg);
   uint32_t ab = fbits(a);
   if (k < KMAX && ab > smid[k]) ++k;
   else if (k > 0 && ab <= smid[k - 1]) --k;
@@ -360,25 +369,137 @@ __device__ __forceinline__ bool group_all(bool v) {
   return b != 0;
 }
 
+// true on every lane when `pred` holds on all lanes of the wave (all lanes
+// are active here): the exact paths below are taken per wave, uniformly
+__device__ __forceinline__ bool wave_all(bool pred) { return __builtin_amdgcn_ballot_w64(!pred) == 0; }
+
+// E2M1 magnitude index of |x| (bits xb) as the number of thresholds passed
+// (the thresholds are non-decreasing); no indexing into t
+__device__ __forceinline__ int rtn_count(uint32_t xb, const uint32_t t[7]) {
+  int m = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) m += xb > t[j] ? 1 : 0;
+  return m;
+}
+
+// element thresholds of E4M3 scale code k under g, formed in binary64 (the
+// same values the LDS tables hold)
+__device__ __forceinline__ void nv_thresholds(int k, double gd, uint32_t t[7]) {
+  const double sv = sf_val<0>(k) * gd;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) t[j] = k > 0 ? thr_bits((double)kMidD[j] * sv, (j & 1) != 0) : 0x7F800000u;
+}
+
+// nearest E4M3 code to a / (T g) (T = 6 or 4), ties to the even code,
+// saturating at 126: binary64 guess corrected by the exact scale midpoints
+__device__ __forceinline__ int select_e4m3_exact(float a, double inv_Tg, double Tg) {
+  int k = select_scale_guess<0>(a, inv_Tg);
+  const uint32_t ab = fbits(a);
+  auto mid = [&](int j) { return thr_bits(0.5 * (sf_val<0>(j) + sf_val<0>(j + 1)) * Tg, (j & 1) != 0); };
+  if (k < 126 && ab > mid(k)) ++k;
+  else if (k > 0 && ab <= mid(k - 1)) --k;
+  return k;
+}
+
+// Exact side of a rounding midpoint.  The midpoint threshold is T = Q g
+// with Q = (midpoint value) * (scale value) exact in FP32 (at most 8
+// significant bits).  Split T = Phi + Plo exactly (Phi = RN(Q g), Plo the
+// FMA residual); near T, |x| - Phi is exact (the operands are within a
+// factor of two), so comparing it with Plo is the exact comparison of |x|
+// with T, equality included.  `odd`: a tie rounds up (to the even neighbour).
+__device__ __forceinline__ bool past_midpoint(float ax, float Q, float g, bool odd) {
+  const float phi = Q * g;
+  const float plo = __builtin_fmaf(Q, g, -phi);
+  const float r1 = ax - phi;
+  return r1 > plo || (r1 == plo && odd);
+}
+
+// Exact codes from low-side codes.  `plo` holds the codes of x * rlo with
+// rlo < 1/(s g): every element's exact code is its low-side code or one
+// magnitude step above (the exact ratio exceeds the low-side ratio by far less
+// than the gap between midpoints).  Step up where |x| is past the midpoint
+// above the low-side magnitude; magnitude 7 (6.0) is the top.
+template <int L>
+__device__ __forceinline__ uint32_t resolve_codes(const float* x, uint32_t plo, float s, float g) {
+  const uint32_t inc = (plo & 0x77777777u) + 0x11111111u;  // magnitude + 1 per nibble
+  uint32_t up = 0;
+  static_for<0, L / 2>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    // half values of the low-side and next magnitudes: their sum is the midpoint
+    const auto vl = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(plo, 0.5f, b);
+    const auto vu = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(inc, 0.5f, b);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * b + h;
+      const uint32_t mag = (plo >> (4 * i)) & 7u;
+      const float mid = fabsf(vl[h]) + vu[h];
+      const bool go = mag != 7u && past_midpoint(fabsf(x[i]), mid * s, g, (mag & 1u) != 0);
+      up |= go ? (0xFu << (4 * i)) : 0u;
+    }
+  });
+  return (plo & ~up) | (((inc & 0x77777777u) | (plo & 0x88888888u)) & up);
+}
+
 // NVFP4 codes of a lane's L elements for scale code k (value s) under global
-// g: bracketed convert, threshold path for blocks it cannot decide.  The
-// bracket is used only for finite blocks with s g well inside the normal range.
-template <int L, int LPB, int FMT>
-__device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, float g, bool finite,
-                                              const Tables<FMT>& T) {
+// g: bracketed convert; when some element of the wave cannot be decided that
+// way (on or near a midpoint), the whole wave resolves its elements exactly
+// from the low-side codes.  The bracket is used only for finite blocks with
+// s g well inside the normal range; a wave with any other block takes the
+// threshold search.
+template <int L, int LPB>
+__device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, float g, bool finite) {
   const float sg = s * g;
   const float r = __builtin_amdgcn_rcpf(sg);  // within 1 ulp of 1 / RN(s g)
-  bool ok = finite && sg > 0x1p-120f && sg < 0x1p120f;
+  const bool ok = finite && sg > 0x1p-120f && sg < 0x1p120f;
   const float rlo = r * (1.0f - 0x1p-20f), rhi = r * (1.0f + 0x1p-20f);
-  bool same;
-  uint32_t packed = encode_bracket<L>(x, rlo, rhi, same);
-  if (!group_all<LPB>(ok && same)) {
-    uint32_t t[7];
+  uint32_t plo = 0, phi = 0;
+  static_for<0, L / 2>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    plo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(plo, x[2 * b] * rlo, x[2 * b + 1] * rlo, 1.0f, b);
+    phi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(phi, x[2 * b] * rhi, x[2 * b + 1] * rhi, 1.0f, b);
+  });
+  if (!wave_all(ok && plo == phi)) {
+    if (wave_all(ok)) {
+      // elements whose two ends differ, one per lane per pass (usually one pass)
+      uint32_t amb = plo ^ phi;
+      while (!wave_all(amb == 0)) {
+        const int sh = amb ? (int)(__builtin_ctz(amb) & ~3) : 0;  // 4 * element index
+        float xi = x[0];
 #pragma unroll
-    for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
-    packed = encode_plain<L>(x, t);
+        for (int j = 1; j < L; ++j) xi = (sh == 4 * j) ? x[j] : xi;
+        const uint32_t mag = (plo >> sh) & 7u;
+        typedef float f2v __attribute__((ext_vector_type(2)));
+        const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(mag | ((mag + 1u) << 4), 0.5f, 0);
+        const bool go = amb != 0 && mag != 7u && past_midpoint(fabsf(xi), (v[0] + v[1]) * s, g, (mag & 1u) != 0);
+        plo += go ? (1u << sh) : 0u;  // magnitude + 1 (at most 7: no carry)
+        amb &= ~(0xFu << sh);
+      }
+    } else {
+      uint32_t t[7];
+      nv_thresholds(k, (double)g, t);
+      plo = 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const uint32_t b = fbits(x[i]);
+        const int m = rtn_count(b & 0x7FFFFFFFu, t);
+        plo |= (m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u) << (4 * i);
+      }
+      return plo;
+    }
   }
-  return packed;
+  return clear_neg_zero(plo);
+}
+
+// nearest E4M3 code to a / (T g) (T = 6 or 4), ties to the even code,
+// saturating at 126: the hardware convert of a * lo (lo < 1/(T g)) gives the
+// exact code or one below; step up where a is past the midpoint
+__device__ __forceinline__ int e4m3_from_low(uint32_t wl_byte, float a, float T, float g) {
+  const int klo = min((int)wl_byte, 126);
+  if (klo == 126) return 126;
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)klo | ((uint32_t)(klo + 1) << 8), 0.5f, false);
+  const float mid = v[0] + v[1];  // exact: at most 5 significant bits
+  return past_midpoint(a, mid * T, g, (klo & 1) != 0) ? klo + 1 : klo;
 }
 
 // block error of a lane's L elements (lane part of the balanced tree);
@@ -423,10 +544,15 @@ template <int FMT, int B, int RULE, bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   constexpr int L = (B == 4) ? 4 : 8;
   constexpr int LPB = B / L;  // lanes per block
-  __shared__ Tables<FMT> T;
+  // LDS tables serve RaZeR and the brute-force search; NVFP4 abs-max and
+  // 4-over-6 and MXFP4 form their rare exact decisions on the fly
+  constexpr bool TABLES = (FMT == RAZER_A || FMT == RAZER_W || RULE == BRUTE);
+  __shared__ Tables<TABLES ? FMT : MXFP4> T;
   const float g = p.global ? *p.global : 1.0f;
-  build_tables<FMT>(T, g, p.special);
-  __syncthreads();
+  if constexpr (TABLES) {
+    build_tables<FMT>(T, g, p.special);
+    __syncthreads();
+  }
 
   const bool chan = p.chan_scale != nullptr;
   const bool had = p.hadamard == 32;
@@ -443,13 +569,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   // encode_nv, and equal codes at both ends are the exact choice
   const bool fast_scale = g > 0x1p-100f && g < 0x1p100f;
   const float r6 = __builtin_amdgcn_rcpf(6.0f * g), r4 = __builtin_amdgcn_rcpf(4.0f * g);
-  const float lo6 = r6 * (1.0f - 0x1p-20f), hi6 = r6 * (1.0f + 0x1p-20f);
-  const float lo4 = r4 * (1.0f - 0x1p-20f), hi4 = r4 * (1.0f + 0x1p-20f);
+  const float lo6 = r6 * (1.0f - 0x1p-20f), lo4 = r4 * (1.0f - 0x1p-20f);
 
   // chunk c = r * cpr + cj; the division happens once, then (r, cj) advance.
   // Each iteration issues the loads of U chunks (c, c + stride, ...) before
   // working on the first, to keep enough bytes in flight per CU.
-  constexpr int U = 4;
+  constexpr int U = (FMT == MXFP4) ? 1 : 2;
   int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   int64_t r0 = CONTIG ? 0 : c / cpr, cj0 = CONTIG ? c : c % cpr;
   const int64_t sr = CONTIG ? 0 : stride / cpr, sc = CONTIG ? stride : stride % cpr;
@@ -502,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       }
       // the convert divides by 2^E exactly (E >= -126: a normal FP32 scale)
       // and rounds to nearest even, which is the format's rounding
-      if (E >= -126 && amax < 0x7F800000u) {
+      if (wave_all(E >= -126 && amax < 0x7F800000u)) {
         packed = 0;
         const float sc = bitsf((uint32_t)(E + 127) << 23);
         static_for<0, L / 2>([&](auto ic) {
@@ -538,30 +663,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       } else {
         const bool finite = amax < 0x7F800000u;
         int k6 = 0, k4 = 0;
-        bool sok = false;
-        if (fast_scale && finite) {
+        if (wave_all(fast_scale && finite)) {
           typedef short s2v __attribute__((ext_vector_type(2)));
           const float a = bitsf(amax);
           const s2v z = {0, 0};
           const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * lo6, a * lo4, 1.0f, false);
-          const s2v chi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * hi6, a * hi4, 1.0f, false);
-          const uint32_t wl = (uint16_t)clo[0], wh = (uint16_t)chi[0];
-          k6 = min((int)(wl & 0xFFu), 126);
-          k4 = min((int)(wl >> 8), 126);
-          sok = k6 == min((int)(wh & 0xFFu), 126) && (RULE != FOUR6 || k4 == min((int)(wh >> 8), 126));
-        }
-        if (!sok) {
-          k6 = select_scale<0>(bitsf(amax), T.smid6, inv6);
-          if constexpr (RULE == FOUR6) k4 = select_scale<0>(bitsf(amax), T.smid4, inv4);
+          const uint32_t wl = (uint16_t)clo[0];
+          k6 = e4m3_from_low(wl & 0xFFu, a, 6.0f, g);
+          if constexpr (RULE == FOUR6) k4 = e4m3_from_low(wl >> 8, a, 4.0f, g);
+        } else {
+          k6 = select_e4m3_exact(bitsf(amax), inv6, 6.0 * (double)g);
+          if constexpr (RULE == FOUR6) k4 = select_e4m3_exact(bitsf(amax), inv4, 4.0 * (double)g);
         }
         if (p.prevent_zero && k6 == 0) k6 = 1;
         const float s6 = e4m3_f32(k6);
-        packed = encode_nv<L, LPB>(x, k6, s6, g, finite, T);
+        packed = encode_nv<L, LPB>(x, k6, s6, g, finite);
         sbyte = (uint8_t)k6;
         if constexpr (RULE == FOUR6) {
           if (p.prevent_zero && k4 == 0) k4 = 1;
           const float s4 = e4m3_f32(k4);
-          uint32_t pk4 = encode_nv<L, LPB>(x, k4, s4, g, finite, T);
+          uint32_t pk4 = encode_nv<L, LPB>(x, k4, s4, g, finite);
           float e6 = group_sum<LPB>(lane_sse<L>(x, packed, s6, g, false, 0.f));
           float e4 = group_sum<LPB>(lane_sse<L>(x, pk4, s4, g, false, 0.f));
           if (e4 < e6) { packed = pk4; sbyte = (uint8_t)k4; }
