@@ -41,6 +41,7 @@ struct GemmParams {
   float w_special[4];
   int64_t M, N, K;
   void* c; int64_t ldc; int c_bf16;
+  int splits;  // K-splits per output tile (1, or > 1 with FP32 atomics into a zeroed C)
 };
 
 struct ChanScaleParams {

@@ -90,37 +90,69 @@ __device__ __forceinline__ uint32_t scale_pair_f16(uint32_t raw4) {
   return (two & (m | (m << 16))) << 7;
 }
 
-// 8 codes -> 8 f16 values value * scale; H selects the block (half of scl2),
-// byte B of raw4 is the block's raw scale byte (RaZeR special selector)
-template <int F, int H, int B>
-__device__ __forceinline__ half8 decode8(uint32_t codes, uint32_t scl2, uint32_t raw4, const float* wspecial) {
+// RaZeR: f16 patterns of special * scale * 2^-8 (or 2^-12) for the two blocks
+// of chunk KC, from the chunk's scale pair and raw scale bytes.  RaZeR-A: the
+// scale byte's top bit picks -5 or +5.  RaZeR-W: its top two bits index the
+// four specials, held as f16 in sp_lo (specials 0, 1) and sp_hi (2, 3).
+// Exact: special (at most 4 significant bits, a multiple of 1/2) times the
+// scale pattern (at most 4 bits, a multiple of 2^-17) is a multiple of 2^-18
+// with at most 8 significant bits.
+template <int F, int KC>
+__device__ __forceinline__ uint32_t special_pair_f16(uint32_t raw4, uint32_t scl2, uint32_t sp_lo, uint32_t sp_hi) {
+  if constexpr (F == RAZER_A) {
+    const half2v five = __builtin_bit_cast(half2v, scl2) * (half2v){(_Float16)5.0f, (_Float16)5.0f};
+    // bytes 2KC, 2KC+1 to the high bytes of the two halves: their top bits are the signs
+    const uint32_t sg = __builtin_amdgcn_perm(0u, raw4, KC ? 0x030C020Cu : 0x010C000Cu) & 0x80008000u;
+    return __builtin_bit_cast(uint32_t, five) ^ sg;
+  } else if constexpr (F == RAZER_W) {
+    const uint32_t i0 = (raw4 >> (16 * KC + 6)) & 3u, i1 = (raw4 >> (16 * KC + 14)) & 3u;
+    // byte selectors of the 8-byte table {sp_hi, sp_lo}: special i at bytes 2i, 2i+1
+    const uint32_t sel = (2u * i0) | ((2u * i0 + 1u) << 8) | ((2u * i1) << 16) | ((2u * i1 + 1u) << 24);
+    const half2v v = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(sp_hi, sp_lo, sel));
+    return __builtin_bit_cast(uint32_t, v * __builtin_bit_cast(half2v, scl2));
+  } else {
+    return 0u;
+  }
+}
+
+// 8 codes -> 8 f16 values value * scale; H selects the block (half of scl2).
+// RaZeR: the convert turns code 0x8 into -0; a second word with code 0x2
+// (+1.0) exactly there and 0 elsewhere is converted too and added times the
+// block's special pattern (spec2, half H): u * special + v is special * scale
+// at those codes (v = -0) and v elsewhere (u = +0), each exact.
+template <int F, int H>
+__device__ __forceinline__ half8 decode8(uint32_t codes, uint32_t scl2, uint32_t spec2) {
   constexpr float kCvt = (F == RAZER_W) ? 4096.0f : 256.0f;
   const _Float16 s16 = __builtin_bit_cast(half2v, scl2)[H];
   const half2v s2 = {s16, s16};
+  uint32_t t = 0;
+  half2v x2 = {};
+  if constexpr (F == RAZER_A || F == RAZER_W) {
+    const uint32_t y = codes ^ 0x88888888u;                          // nibble 0 where the code is 0x8
+    const uint32_t nz = ((y & 0x77777777u) + 0x77777777u) | y;       // bit 3: nibble != 0
+    t = (~nz & 0x88888888u) >> 2;                                    // 0x2 where the code is 0x8
+    const _Float16 x16 = __builtin_bit_cast(half2v, spec2)[H];
+    x2 = (half2v){x16, x16};
+  }
   half8 out;
   static_for<0, 4>([&](auto ic) {
     constexpr int b = decltype(ic)::value;
     half2v v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, kCvt, b);
     v = v * s2;  // exact: value * scale
+    if constexpr (F == RAZER_A || F == RAZER_W) {
+      const half2v u = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, kCvt, b);
+      v = __builtin_elementwise_fma(u, x2, v);
+    }
     out[2 * b] = v[0];
     out[2 * b + 1] = v[1];
   });
-  if constexpr (F == RAZER_A || F == RAZER_W) {
-    const uint32_t sb = (raw4 >> (8 * B)) & 0xFFu;
-    float v = (F == RAZER_A) ? ((sb & 0x80u) ? -5.0f : 5.0f) : wspecial[sb >> 6];
-    const _Float16 vs = (_Float16)(v * kCvt) * s16;  // exact
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (((codes >> (4 * i)) & 15u) == 8u) out[i] = vs;
-  }
   return out;
 }
 
 // ---------------------------------------------------------------- tile order
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int bid, int& tm, int& tn) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
   // workgroup bid runs on XCD bid % 8: give every XCD a contiguous range of tiles
   const int q = T / kXcds, r = T % kXcds;
   const int x = bid % kXcds, loc = bid / kXcds;
@@ -325,8 +357,8 @@ __device__ __forceinline__ void sched_step() {
 struct NvRegs {
   uint4 ca0[4], cw0[4], ca1[4], cw1[4];
   uint32_t ra[4], rw[4];     // stage scale dwords (read one stage ahead)
-  uint32_t qa[4], qw[4];     // the current stage's dwords for chunk 1 (RaZeR)
-  uint32_t pa0[4], pw0[4], pa1[4], pw1[4];
+  uint32_t pa0[4], pw0[4], pa1[4], pw1[4];  // f16 scale pairs per chunk
+  uint32_t xa0[4], xw0[4], xa1[4], xw1[4];  // f16 special pairs per chunk (RaZeR)
 };
 
 struct NvAddr {   // per-lane LDS byte offsets within a stage buffer
@@ -350,15 +382,15 @@ __device__ __forceinline__ void read_scales(const uint8_t* buf, const NvAddr& ad
   }
 }
 
-// decode of MFMA step J (0..3) of chunk KC: codes word J, scale block J / 2
-template <int FA, int FW, int KC, int J>
+// decode of MFMA step J (0..3) of a chunk: codes word J, scale block J / 2
+template <int FA, int FW, int J>
 __device__ __forceinline__ void decode_step(const uint4 (&ca)[4], const uint4 (&cw)[4], const uint32_t (&pa)[4],
-                                            const uint32_t (&pw)[4], const uint32_t (&qa)[4], const uint32_t (&qw)[4],
-                                            const float* wspecial, half8 (&a)[4], half8 (&b)[4]) {
+                                            const uint32_t (&pw)[4], const uint32_t (&xa)[4], const uint32_t (&xw)[4],
+                                            half8 (&a)[4], half8 (&b)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[i] = decode8<FA, J / 2, 2 * KC + J / 2>(u4_get(ca[i], J), pa[i], qa[i], nullptr);
-    b[i] = decode8<FW, J / 2, 2 * KC + J / 2>(u4_get(cw[i], J), pw[i], qw[i], wspecial);
+    a[i] = decode8<FA, J / 2>(u4_get(ca[i], J), pa[i], xa[i]);
+    b[i] = decode8<FW, J / 2>(u4_get(cw[i], J), pw[i], xw[i]);
   }
 }
 
@@ -416,12 +448,14 @@ constexpr bool plan_valid() {
 // Every LDS read is used at least two steps after it is issued.
 template <int FA, int FW, class P = NvPlan>
 __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
-                                        f32x16 (&acc)[4][4]) {
-  constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);  // special values need raw scale bytes
+                                        int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
+  constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);  // special values in the decode
   static_assert(plan_valid<P>(), "staging plan");
   Loader<false> L;
   L.init(p, m0, n0);
-  const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
+  // this workgroup's stages [sbeg, send) of the K loop; local stage s starts
+  // at element kb + s * BK, and the first nfull local stages lie inside K
+  const int64_t kb = sbeg * BK, nstages = send - sbeg, nfull = min(send, p.K / BK) - sbeg;
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
   NvAddr ad;
 #pragma unroll
@@ -436,24 +470,43 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
 
   Stage<false> st;
   auto gload = [&](int64_t stg) {
-    if (stg < nfull && L.vec_scales) load_fast<false>(L, stg * BK, st);
-    else load_any<false>(L, stg * BK, st);
+    if (stg < nfull && L.vec_scales) load_fast<false>(L, kb + stg * BK, st);
+    else load_any<false>(L, kb + stg * BK, st);
   };
   gload(0);
   store_stage<false>(smem, st);
   if (nstages > 1) gload(1);
   lds_barrier();
+  // RaZeR-W specials as f16 (exact: multiples of 1/2 up to 7.5), two per word
+  const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
+  const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
   NvRegs R;
   read_scales(smem, ad, R.ra, R.rw);
   read_codes(smem, ad, 0, R.ca0, R.cw0);
   if constexpr (P::read1 == 7) read_codes(smem, ad, 1, R.ca1, R.cw1);
+  // f16 scale (and special) pairs of chunk KC of the dwords in R.ra / R.rw
+  auto prep_a = [&](auto kc_tag, uint32_t (&pa)[4], uint32_t (&xa)[4]) {
+    constexpr int KC = decltype(kc_tag)::value;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
-    R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
-  }
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = scale_pair_f16<FA, KC>(R.ra[i]);
+      if constexpr (RZ) xa[i] = special_pair_f16<FA, KC>(R.ra[i], pa[i], sp_lo, sp_hi);
+    }
+  };
+  auto prep_w = [&](auto kc_tag, uint32_t (&pw)[4], uint32_t (&xw)[4]) {
+    constexpr int KC = decltype(kc_tag)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = scale_pair_f16<FW, KC>(R.rw[i]);
+      if constexpr (RZ) xw[i] = special_pair_f16<FW, KC>(R.rw[i], pw[i], sp_lo, sp_hi);
+    }
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  prep_a(K0{}, R.pa0, R.xa0);
+  prep_w(K0{}, R.pw0, R.xw0);
   half8 da[2][4], db[2][4];
-  decode_step<FA, FW, 0, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[0], db[0]);
+  decode_step<FA, FW, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[0], db[0]);
 
   // FAST: stages s with s + 2 < nfull and word-aligned scales (branch-free);
   // the others check whether stage s+1 / s+2 exist.  On the last stage the
@@ -470,21 +523,11 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
         if (FAST || s + 1 < nstages) store_stage<false, st0, st1>(nbuf, st);
       }
       if constexpr (ld0 < ld1) {
-        if constexpr (FAST) load_fast<false, ld0, ld1>(L, (s + 2) * BK, st);
+        if constexpr (FAST) load_fast<false, ld0, ld1>(L, kb + (s + 2) * BK, st);
         else if (ld0 == 0 && s + 2 < nstages) gload(s + 2);
       }
-      if constexpr (t == 0 || t == 1) {  // chunk-1 scale pairs, A at step 0, W at step 1
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (t == 0) {
-            R.pa1[i] = scale_pair_f16<FA, 1>(R.ra[i]);
-            if constexpr (RZ) R.qa[i] = R.ra[i];
-          } else {
-            R.pw1[i] = scale_pair_f16<FW, 1>(R.rw[i]);
-            if constexpr (RZ) R.qw[i] = R.rw[i];
-          }
-        }
-      }
+      if constexpr (t == 0) prep_a(K1{}, R.pa1, R.xa1);  // chunk-1 pairs, A at step 0, W at step 1
+      if constexpr (t == 1) prep_w(K1{}, R.pw1, R.xw1);
       if constexpr (t == P::read1) {
         if constexpr (t == 7) read_codes(nbuf, ad, 1, R.ca1, R.cw1);
         else read_codes(cbuf, ad, 1, R.ca1, R.cw1);
@@ -493,20 +536,15 @@ __device__ __forceinline__ void nv_tile(const GemmParams& p, int64_t m0, int64_t
         read_scales(nbuf, ad, R.ra, R.rw);
         read_codes(nbuf, ad, 0, R.ca0, R.cw0);
       }
-      if constexpr (t == 4 || t == 5) {  // next stage's chunk-0 scale pairs
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (t == 4) R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
-          else R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
-        }
-      }
+      if constexpr (t == 4) prep_a(K0{}, R.pa0, R.xa0);  // next stage's chunk-0 pairs
+      if constexpr (t == 5) prep_w(K0{}, R.pw0, R.xw0);
       // decode of step t + 1
       if constexpr (t < 3)
-        decode_step<FA, FW, 0, t + 1>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+        decode_step<FA, FW, t + 1>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[cur ^ 1], db[cur ^ 1]);
       else if constexpr (t < 7)
-        decode_step<FA, FW, 1, t - 3>(R.ca1, R.cw1, R.pa1, R.pw1, R.qa, R.qw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+        decode_step<FA, FW, t - 3>(R.ca1, R.cw1, R.pa1, R.pw1, R.xa1, R.xw1, da[cur ^ 1], db[cur ^ 1]);
       else
-        decode_step<FA, FW, 0, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.ra, R.rw, p.w_special, da[cur ^ 1], db[cur ^ 1]);
+        decode_step<FA, FW, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[cur ^ 1], db[cur ^ 1]);
       mfma_step(da[cur], db[cur], acc);
       if constexpr (FAST) {
         constexpr int ndsr = (t == 3 ? 16 : 0) + (t == P::read1 ? 8 : 0);
@@ -570,7 +608,7 @@ struct MxPlan {
 //           dwords and chunk-0 codes; issue the remaining global loads.
 // Chunk-0 and chunk-1 codes are read two steps before use.
 __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm, int wn,
-                                        f32x16 (&acc)[4][4]) {
+                                        int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
   Loader<true> L;
   L.init(p, m0, n0);
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
@@ -584,11 +622,11 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
   }
   ad.sa = 2 * kCodeBytes + (wm * 4 * 64 + lane) * 4;
   ad.sw = 2 * kCodeBytes + kScaleBytes + (wn * 4 * 64 + lane) * 4;
-  const int64_t nstages = (p.K + BK - 1) / BK, nfull = p.K / BK;
+  const int64_t kb = sbeg * BK, nstages = send - sbeg, nfull = min(send, p.K / BK) - sbeg;
   Stage<true> st[2];
   auto gload = [&](int64_t stg, Stage<true>& dst) {
-    if (stg < nfull && L.vec_scales) load_fast<true>(L, stg * BK, dst);
-    else load_any<true>(L, stg * BK, dst);
+    if (stg < nfull && L.vec_scales) load_fast<true>(L, kb + stg * BK, dst);
+    else load_any<true>(L, kb + stg * BK, dst);
   };
   gload(0, st[0]);
   store_stage<true>(smem, st[0]);
@@ -613,7 +651,7 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
     if constexpr (FAST) sched_mx_step<6, 0, 4>();
     // step 1
     if (FAST || s + 1 < nstages) store_stage<true, 6, kItems>(nbuf, sg);
-    if constexpr (FAST) load_fast<true, 0, MxPlan::load_at[1]>(L, (s + 3) * BK, sg);
+    if constexpr (FAST) load_fast<true, 0, MxPlan::load_at[1]>(L, kb + (s + 3) * BK, sg);
     else if (s + 3 < nstages) gload(s + 3, sg);
     mx_mfma_half<0, 2>(ca0, cw0, sa, sw, acc);
     if constexpr (FAST) sched_mx_step<6, MxPlan::load_at[1], 0>();
@@ -626,11 +664,11 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
     }
     read_scales(nbuf, ad, sa, sw);
     read_codes(nbuf, ad, 0, ca0, cw0);
-    if constexpr (FAST) load_fast<true, MxPlan::load_at[1], MxPlan::load_at[2]>(L, (s + 3) * BK, sg);
+    if constexpr (FAST) load_fast<true, MxPlan::load_at[1], MxPlan::load_at[2]>(L, kb + (s + 3) * BK, sg);
     mx_mfma_half<1, 0>(ca1, cw1, qa, qw, acc);
     if constexpr (FAST) sched_mx_step<0, MxPlan::load_at[2] - MxPlan::load_at[1], 8>();
     // step 3
-    if constexpr (FAST) load_fast<true, MxPlan::load_at[2], kItems>(L, (s + 3) * BK, sg);
+    if constexpr (FAST) load_fast<true, MxPlan::load_at[2], kItems>(L, kb + (s + 3) * BK, sg);
     mx_mfma_half<1, 2>(ca1, cw1, qa, qw, acc);
     if constexpr (FAST) sched_mx_step<0, kItems - MxPlan::load_at[2], 0>();
   };
@@ -655,8 +693,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_tile_kernel(GemmParams p) {
   constexpr bool MX = (FA == MXFP4);
   __shared__ __align__(16) uint8_t smem[kNbuf * kBufBytes];
+  // workgroup = (tile, K-split); split s owns stages [s * per, (s + 1) * per)
+  const int split = (int)(blockIdx.x % (unsigned)p.splits);
   int tm, tn;
-  tile_coords(p.M, p.N, tm, tn);
+  tile_coords(p.M, p.N, (int)(blockIdx.x / (unsigned)p.splits), tm, tn);
+  const int64_t nst = (p.K + BK - 1) / BK, per = (nst + p.splits - 1) / p.splits;
+  const int64_t sbeg = min(nst, split * per), send = min(nst, sbeg + per);
+  if (sbeg >= send) return;  // no stages left for this split (uniform across the workgroup)
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -667,8 +710,8 @@ void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-  if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, acc);
-  else mx_tile(p, m0, n0, smem, wm, wn, acc);
+  if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+  else mx_tile(p, m0, n0, smem, wm, wn, sbeg, send, acc);
 
   const float ga = p.a_global ? *p.a_global : 1.0f;
   const float gw = p.w_global ? *p.w_global : 1.0f;
@@ -690,6 +733,8 @@ void gemm_tile_kernel(GemmParams p) {
           uint32_t u = __float_as_uint(v);
           u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
           ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
+        } else if (p.splits > 1) {
+          atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
         } else {
           ((float*)p.c)[row * p.ldc + col] = v;
         }
@@ -698,11 +743,52 @@ void gemm_tile_kernel(GemmParams p) {
   }
 }
 
+// FP32 C rows [0, M) x columns [0, N) <- 0 (ahead of split-K accumulation)
+__global__ __launch_bounds__(256) void zero_c_kernel(float* c, int64_t M, int64_t N, int64_t ldc) {
+  const int64_t total = M * N, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) c[(i / N) * ldc + i % N] = 0.0f;
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// K-splits for an FP32 output with too few tiles to fill the chip: the count
+// that minimises (rounds of workgroups over the CUs) x (stages per split),
+// at most 4 (each split adds one read-modify-write of C)
+int choose_splits(const GemmParams& p, int64_t T) {
+  const int cus = device_cus();
+  if (p.c_bf16 || T >= cus) return 1;
+  const int64_t nst = (p.K + BK - 1) / BK;
+  int best = 1;
+  int64_t best_cost = ((T + cus - 1) / cus) * nst;
+  for (int sp = 2; sp <= 4 && sp <= nst; ++sp) {
+    const int64_t cost = ((T * sp + cus - 1) / cus) * ((nst + sp - 1) / sp);
+    if (cost < best_cost) { best = sp; best_cost = cost; }
+  }
+  return best;
+}
+
 template <int FA, int FW>
-hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
-  const int64_t T = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (p.c_bf16) hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, true>), dim3((unsigned)T), dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, false>), dim3((unsigned)T), dim3(kThreads), 0, s, p);
+hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
+  const int64_t T = ((p0.M + BM - 1) / BM) * ((p0.N + BN - 1) / BN);
+  GemmParams p = p0;
+  p.splits = choose_splits(p0, T);
+  if (p.splits > 1) {
+    const int64_t need = (p.M * p.N + 255) / 256, blocks = need < 4096 ? need : 4096;
+    hipLaunchKernelGGL(zero_c_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
+  }
+  const unsigned grid = (unsigned)(T * p.splits);
+  if (p.c_bf16) hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, false>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
