@@ -55,7 +55,7 @@ class Prefill:
     name = "prefill_hybrid_layer"
     M, K, NS = 32768, 5120, (10240, 17408, 5120)
     compute_dtype = "f16"
-    gemm_kernel = "gemm_nv_kernel"
+    gemm_kernel = "gemm_tile_kernel"
     quant_kernel = "quantize_kernel"
 
     def __init__(self, B):
@@ -101,7 +101,7 @@ class MxLinear:
     name = "mxfp4_linear"
     M, K, N = 4096, 4096, 14336
     compute_dtype = "fp4"
-    gemm_kernel = "gemm_mx_kernel"
+    gemm_kernel = "gemm_tile_kernel"
     quant_kernel = "quantize_kernel"
 
     def __init__(self, B):
@@ -141,7 +141,7 @@ class RazerDecode:
     name = "razer_decode"
     M, K, N = 128, 5120, 17408
     compute_dtype = "f16"
-    gemm_kernel = "gemm_nv_kernel"
+    gemm_kernel = "gemm_tile_kernel"
     quant_kernel = "quantize_kernel"
 
     def __init__(self, B, M=128):
@@ -284,6 +284,67 @@ def traffic_record(kernel_source: str):
     return rec
 
 
+# ---------------------------------------------------------------- profile helpers
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """A plain elementwise kernel of known traffic (reads and writes 1 GiB of
+    FP32 per launch), for scaling the HBM counters of rocprofv3 --pmc runs"""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("[bench] copy probe done")
+
+
+def summarize_stats(stats_csv: str, out_md: str, title: str, command: str) -> None:
+    """rocprofv3 kernel_stats.csv -> short markdown table"""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\nCommand (from the repository root on the GPU box):\n\n```\n{command}\n```\n\n")
+        f.write("| kernel | calls | average (us) | min (us) | max (us) | share (%) |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"].replace("fp4q::(anonymous namespace)::", "").replace("void ", "")
+            name = name.split("(")[0] if "at::native" not in name else name[:60]
+            f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                    f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |\n")
+
+
+def _counter_means(csv_path: str, counter: str, name_part: str):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {name_part!r} in {csv_path}")
+    return float(np.mean(vals)), len(vals)
+
+
+def traffic_from_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                     out_json: str, kernel: str = "gemm_tile_kernel") -> dict:
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe"""
+    fk, nf = _counter_means(fetch_csv, "FETCH_SIZE", kernel)
+    wk, nw = _counter_means(write_csv, "WRITE_SIZE", kernel)
+    cf, _ = _counter_means(copy_fetch_csv, "FETCH_SIZE", "neg")
+    cw, _ = _counter_means(copy_write_csv, "WRITE_SIZE", "neg")
+    f_scale = cf * 1024.0 / COPY_PROBE_BYTES   # counter KiB per true KiB
+    w_scale = cw * 1024.0 / COPY_PROBE_BYTES
+    fetch_b = fk * 1024.0 / f_scale
+    write_b = wk * 1024.0 / w_scale
+    src = open(os.path.join(ROOT, "block_scaled_fp4_e4m3_amd", "csrc", "gemm.hip"), "rb").read()
+    rec = {"workload": workload, "kernel": kernel, "source_sha256": hashlib.sha256(src).hexdigest(),
+           "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+           "bytes_per_launch": fetch_b + write_b, "dispatches": {"fetch": nf, "write": nw},
+           "copy_probe_scale": {"fetch": f_scale, "write": w_scale}}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +352,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run the counter-scaling copy kernel and exit")
+    ap.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--traffic-record", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT_JSON"),
+                    help="HBM bytes per GEMM launch of --workload from rocprofv3 --pmc CSVs, then exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.traffic_record:
+        wl_name = {"prefill": "prefill_hybrid_layer_M32768_K5120_N10240-17408-5120",
+                   "mxfp4_linear": "mxfp4_linear_M4096_K4096_N14336",
+                   "razer_decode": "razer_decode_M128_K5120_N17408"}[args.workload]
+        print(json.dumps(traffic_from_pmc(wl_name, *args.traffic_record)))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -303,6 +379,9 @@ def main():
     import block_scaled_fp4_e4m3_amd as B
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     wl = WORKLOADS[args.workload](B)
     log(f"[bench] warmup {args.warmup}")

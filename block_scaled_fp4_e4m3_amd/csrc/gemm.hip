@@ -743,10 +743,17 @@ void gemm_tile_kernel(GemmParams p) {
   }
 }
 
-// FP32 C rows [0, M) x columns [0, N) <- 0 (ahead of split-K accumulation)
+// FP32 C rows [0, M) x columns [0, N) <- 0 (ahead of split-K accumulation);
+// rows are 16-byte aligned (pitch and base), four columns per thread
 __global__ __launch_bounds__(256) void zero_c_kernel(float* c, int64_t M, int64_t N, int64_t ldc) {
-  const int64_t total = M * N, stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) c[(i / N) * ldc + i % N] = 0.0f;
+  const int64_t col = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (col >= N) return;
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
+    float* dst = c + row * ldc + col;
+    if (col + 4 <= N) *(float4*)dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    else
+      for (int64_t j = 0; j < N - col; ++j) dst[j] = 0.0f;
+  }
 }
 
 int device_cus() {
@@ -783,8 +790,8 @@ hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
   GemmParams p = p0;
   p.splits = choose_splits(p0, T);
   if (p.splits > 1) {
-    const int64_t need = (p.M * p.N + 255) / 256, blocks = need < 4096 ? need : 4096;
-    hipLaunchKernelGGL(zero_c_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
+    const unsigned gx = (unsigned)((p.N + 1023) / 1024), gy = (unsigned)(p.M < 1024 ? p.M : 1024);
+    hipLaunchKernelGGL(zero_c_kernel, dim3(gx, gy), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
   }
   const unsigned grid = (unsigned)(T * p.splits);
   if (p.c_bf16) hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, true>), dim3(grid), dim3(kThreads), 0, s, p);

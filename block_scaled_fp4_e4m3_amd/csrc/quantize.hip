@@ -881,7 +881,13 @@ int grid_for(int64_t work_items, int64_t cap = 256 * 16) {  // default: 16 workg
 template <int FMT, int B, int RULE>
 hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   constexpr int L = (B == 4) ? 4 : 8;
-  int grid = grid_for(p.rows * (p.cols / L));
+  const int64_t chunks = p.rows * (p.cols / L);
+  int grid = grid_for(chunks);
+  // kernels that build LDS tables per workgroup: at least 8 chunks per thread
+  if (FMT == RAZER_A || FMT == RAZER_W || RULE == BRUTE) {
+    const int64_t cap = (chunks + 256 * 8 - 1) / (256 * 8);
+    if (grid > cap) grid = (int)(cap < 1 ? 1 : cap);
+  }
   // the brute-force search is compute-bound: one addressing variant suffices
   const bool contig = RULE != BRUTE && p.ld == p.cols && p.chan_scale == nullptr;
   if (contig) {
