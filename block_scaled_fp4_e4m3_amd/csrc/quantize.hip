@@ -273,14 +273,16 @@ __device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, c
       }
     }
     // cross-lane stages h = L .. 16 with partner lane ^ (h / L)
+    // butterfly with the partner lane: the lower lane keeps x + o, the upper
+    // o - x, written as o + (+-x) (the same IEEE operations)
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int d = 1; d < 32 / L; d *= 2) {
-      const bool lower = (lane & d) == 0;
+      const uint32_t neg = (lane & d) ? 0x80000000u : 0u;
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        float o = lane_xor_f(x[i], d);
-        x[i] = lower ? (x[i] + o) : (o - x[i]);
+        const float o = lane_xor_f(x[i], d);
+        x[i] = o + bitsf(fbits(x[i]) ^ neg);
       }
     }
     const float c = bitsf(0x3E3504F3u);  // RN32(2^-2.5)
