@@ -799,12 +799,237 @@ hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- small M
+// M <= 32 (decode shapes), NVFP4 family, K a multiple of 512.  Each wave owns
+// 32 output columns and all M rows as one 32 x 32 MFMA accumulator (rows past
+// M are computed from the clamped last row and never stored).  A, at most 32
+// rows, is decoded once per workgroup into LDS in fragment order, a window of
+// kSmWin 64-element chunks at a time.  Each wave streams its 32 weight rows
+// from global memory through a ring of kSmRing chunks in registers; one
+// 16-byte load per lane brings a ring turn's scales (4 blocks of each of 4
+// chunks of its row) a turn ahead, and each turn also loads one chunk of the
+// next window's A.  The decode and the K permutation are those of the tile
+// kernel.  The splits of K, whole windows each, add into a zero-filled FP32 C
+// with atomics.
+//
+// No load is conditional: windows are full, the last window is peeled and its
+// last turn issues no refills.  Loads complete in issue order, and with the
+// same loads on every path the compiler's wait for a ring slot counts exactly
+// the loads issued after it, so the ring never drains.
+constexpr int kSmallM = 32;
+constexpr int kSmRing = 4;  // chunks per ring turn, one scale load each turn
+#ifndef FP4Q_SM_WIN
+#define FP4Q_SM_WIN 8
+#endif
+#ifndef FP4Q_SM_WGS_PER_CU
+#define FP4Q_SM_WGS_PER_CU 4
+#endif
+constexpr int kSmWin = FP4Q_SM_WIN;
+static_assert(kSmWin % kSmRing == 0 && kSmWin % 4 == 0, "a window is whole ring turns and wave rounds");
+constexpr int kSmTurns = kSmWin / kSmRing;  // ring turns per window = A chunks a wave decodes per window
+static_assert(kSmTurns == kSmWin / 4, "one A chunk per wave per turn");
+
+// buffer views of one operand for the rows [r0, r0 + 32)
+struct SmRows {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  int voff_c, voff_s;  // byte offsets of this lane's half chunk and scale row
+};
+
+__device__ __forceinline__ SmRows sm_rows(const uint8_t* codes, const uint8_t* scales, int64_t r0, int64_t rows,
+                                          int64_t K, int r32, int kh) {
+  const int64_t rowbytes = K / 2, nblk = K / 16;
+  const int64_t r = min((int64_t)r32, rows - 1 - r0);
+  SmRows v;
+  v.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + r0 * rowbytes), (short)0, -1, (int)kRsrcWord3);
+  v.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + r0 * nblk), (short)0, -1, (int)kRsrcWord3);
+  v.voff_c = (int)(r * rowbytes + kh * 16);
+  v.voff_s = (int)(r * nblk);
+  return v;
+}
+
+// chunk kc of an A row: 32 codes and the scale bytes of the lane's two blocks
+__device__ __forceinline__ void sm_load_a(const SmRows& v, int64_t kc, int kh, uint4& c, uint32_t& sc) {
+  c = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(v.codes, v.voff_c, (int)(kc * 32), 0));
+  sc = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.voff_s + 2 * kh, (int)(kc * 4), 0);
+}
+
+// chunk kc of a W row: the lane's 32 codes
+__device__ __forceinline__ uint4 sm_codes(const SmRows& v, int64_t kc) {
+  return as_uint4(__builtin_amdgcn_raw_buffer_load_b128(v.codes, v.voff_c, (int)(kc * 32), 0));
+}
+
+// the 16 scale bytes of chunks kc .. kc + 3 of a W row (kc a multiple of 4)
+__device__ __forceinline__ uint4 sm_scales4(const SmRows& v, int64_t kc) {
+  return as_uint4(__builtin_amdgcn_raw_buffer_load_b128(v.scales, v.voff_s, (int)(kc * 4), 0));
+}
+
+template <int F>
+__device__ __forceinline__ void sm_decode(const uint4& c, uint32_t sc, uint32_t sp_lo, uint32_t sp_hi, half8 (&out)[4]) {
+  const uint32_t pr = scale_pair_f16<F, 0>(sc);
+  uint32_t x = 0;
+  if constexpr (F == RAZER_A || F == RAZER_W) x = special_pair_f16<F, 0>(sc, pr, sp_lo, sp_hi);
+  static_for<0, 4>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    out[J] = decode8<F, J / 2>(u4_get(c, J), pr, x);
+  });
+}
+
+// chunks per split: whole windows, as even as that allows
+__host__ __device__ inline int64_t sm_split_len(int64_t nch, int64_t splits) {
+  const int64_t q = (nch + splits - 1) / splits;
+  return (q + kSmWin - 1) / kSmWin * kSmWin;
+}
+
+template <int FA, int FW, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(GemmParams p) {
+  __shared__ __align__(16) half8 adec[kSmWin][4][64];
+  const int split = (int)(blockIdx.x % (unsigned)p.splits);
+  const int64_t slab = blockIdx.x / (unsigned)p.splits;
+  // the wave index is uniform: read it into a scalar so that the buffer
+  // views built from it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
+  const int64_t n0 = slab * 128 + wave * 32;
+  const bool live = n0 < p.N;  // waves past N read row N - 1 and decode their share of A
+  const int64_t nch = p.K / 64, per = sm_split_len(nch, p.splits);
+  const int64_t cb = split * per, ce = min(nch, cb + per);  // cb < ce: every split is used
+  const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
+  const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
+  const SmRows av = sm_rows(p.a_codes, p.a_scales, 0, p.M, p.K, r32, kh);
+  const SmRows wv = sm_rows(p.w_codes, p.w_scales, live ? n0 : p.N - 1, p.N, p.K, r32, kh);
+
+  f32x16 acc = {};
+  uint4 rc[kSmRing], ca[kSmTurns], scur, snext;
+  uint32_t sa[kSmTurns];
+  static_for<0, kSmTurns>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    sm_load_a(av, cb + wave + 4 * j, kh, ca[j], sa[j]);
+  });
+  __builtin_amdgcn_sched_barrier(0);  // A first, then the ring in slot order
+  scur = sm_scales4(wv, cb);
+  static_for<0, kSmRing>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    rc[u] = sm_codes(wv, cb + u);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  snext = sm_scales4(wv, min(cb + kSmRing, ce - kSmRing));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // turn J of the window at wb: chunks g0 .. g0 + 3
+  auto turn = [&](int64_t wb, auto jc, auto refill, auto next_a) {
+    constexpr int J = decltype(jc)::value;
+    const int64_t g0 = wb + kSmRing * J;
+    if constexpr (decltype(next_a)::value) {
+      sm_load_a(av, wb + kSmWin + wave + 4 * J, kh, ca[J], sa[J]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    static_for<0, kSmRing>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const uint32_t sw = u4_get(scur, u) >> (16 * kh);
+      // decode the slot, then refill it: the refill's registers are then free
+      // and stay the slot's own, with no copies around the loop
+      half8 b[4];
+      if (live) sm_decode<FW>(rc[u], sw, sp_lo, sp_hi, b);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(refill)::value) rc[u] = sm_codes(wv, g0 + kSmRing + u);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+        static_for<0, 4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(adec[kSmRing * J + u][I][lane], b[I], acc, 0, 0, 0);
+        });
+      }
+    });
+    if constexpr (decltype(refill)::value) {
+      scur = snext;
+      snext = sm_scales4(wv, min(g0 + 2 * kSmRing, ce - kSmRing));
+    }
+  };
+  auto window = [&](int64_t wb, auto lastw) {
+    constexpr bool LW = decltype(lastw)::value;
+    lds_barrier();  // the previous window's fragments have been read
+    static_for<0, kSmTurns>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      half8 d[4];
+      sm_decode<FA>(ca[j], sa[j], sp_lo, sp_hi, d);
+      static_for<0, 4>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        adec[wave + 4 * j][I][lane] = d[I];
+      });
+    });
+    lds_barrier();
+    static_for<0, kSmTurns>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      turn(wb, jc, std::integral_constant<bool, !(LW && j == kSmTurns - 1)>{}, std::integral_constant<bool, !LW>{});
+    });
+  };
+  int64_t wb = cb;
+  for (; wb + kSmWin < ce; wb += kSmWin) window(wb, std::false_type{});
+  window(wb, std::true_type{});
+  if (!live) return;
+
+  const float gg = (p.a_global ? *p.a_global : 1.0f) * (p.w_global ? *p.w_global : 1.0f);
+  const int64_t col = n0 + r32;
+  if (col >= p.N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = (r / 4) * 8 + kh * 4 + (r % 4);
+    if (row >= p.M) continue;
+    const float v = gg * acc[r];
+    if constexpr (OUT_BF16) {
+      uint32_t u = __float_as_uint(v);
+      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+      ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
+    } else if (p.splits > 1) {
+      atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
+    } else {
+      ((float*)p.c)[row * p.ldc + col] = v;
+    }
+  }
+}
+
+// the small-M kernel takes K a multiple of 64 kSmWin (whole windows) and
+// operands aligned for its 16-byte code and scale loads
+bool small_m_fits(const GemmParams& p) {
+  const uintptr_t a = (uintptr_t)p.a_codes | (uintptr_t)p.w_codes | (uintptr_t)p.a_scales | (uintptr_t)p.w_scales;
+  return p.M <= kSmallM && p.K % (64 * kSmWin) == 0 && (a & 15u) == 0;
+}
+
+template <int FA, int FW>
+hipError_t launch_small_m(const GemmParams& p0, hipStream_t s) {
+  GemmParams p = p0;
+  const int64_t slabs = (p.N + 127) / 128, nch = p.K / 64;
+  // FP32 output: splits of K for about FP4Q_SM_WGS_PER_CU workgroups per CU
+  int64_t sp = 1;
+  if (!p.c_bf16) {
+    sp = (FP4Q_SM_WGS_PER_CU * (int64_t)device_cus() + slabs - 1) / slabs;
+    if (sp > nch / kSmWin) sp = nch / kSmWin;
+    if (sp < 1) sp = 1;
+    sp = (nch + sm_split_len(nch, sp) - 1) / sm_split_len(nch, sp);  // splits in use
+  }
+  p.splits = (int)sp;
+  if (sp > 1) {
+    const unsigned gx = (unsigned)((p.N + 1023) / 1024), gy = (unsigned)(p.M < 1024 ? p.M : 1024);
+    hipLaunchKernelGGL(zero_c_kernel, dim3(gx, gy), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
+  }
+  const unsigned grid = (unsigned)(slabs * sp);
+  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int FA, int FW>
+hipError_t launch_nv(const GemmParams& p, hipStream_t s) {
+  if (small_m_fits(p)) return launch_small_m<FA, FW>(p, s);
+  return launch_tile<FA, FW>(p, s);
+}
+
 template <int FA>
 hipError_t launch_nv_a(int fw, const GemmParams& p, hipStream_t s) {
   switch (fw) {
-    case RAZER_A: return launch_tile<FA, RAZER_A>(p, s);
-    case RAZER_W: return launch_tile<FA, RAZER_W>(p, s);
-    default: return launch_tile<FA, NVFP4>(p, s);
+    case RAZER_A: return launch_nv<FA, RAZER_A>(p, s);
+    case RAZER_W: return launch_nv<FA, RAZER_W>(p, s);
+    default: return launch_nv<FA, NVFP4>(p, s);
   }
 }
 

@@ -70,6 +70,26 @@ def test_gemm_small(B, fa, fw, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
+# decode shapes (M <= 32): several K splits and A windows (K a multiple of
+# 512), the smallest K, waves past N, and K that are not multiples of 512
+# (taken by the tile kernel)
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w"), ("nvfp4", "razer_a")])
+@pytest.mark.parametrize("M,N,K", [(5, 200, 2560), (32, 129, 4096), (1, 384, 4096), (2, 70, 512), (3, 64, 1040),
+                                   (9, 150, 2080)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_decode_shapes(B, fa, fw, M, N, K, out_dtype):
+    a = datagen.student_t((M, K), 700 + M, 4.0)
+    w = datagen.normal((N, K), 800 + N, 0.02)
+    sp = SPECIAL if fw == "razer_w" else None
+    ca, sa, ga = oquant(a, fa)
+    cw, sw, gw = oquant(w, fw, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, M, N, K)
+    case(f"gemm decode {fa}x{fw} {M}x{N}x{K} {out_dtype}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp, out_dtype)
+    tol = TOL if out_dtype == "f32" else 8e-3
+    assert rel_fro(got, ref) <= tol
+
+
 @pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("mxfp4", "mxfp4"), ("razer_a", "razer_w")])
 def test_gemm_exact_regime_bitwise(B, fa, fw):
     # g = 1, every block scale 1 (E4M3 code 56, E8M0 127, E3M3 code 24), K <= 256:
