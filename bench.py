@@ -15,7 +15,8 @@ A step is one pass of the whole path over one batch of synthetic input:
                      channel scale + block-Hadamard + MXFP4 quantization, then
                      the 4096 x 14336 x 4096 MXFP4 GEMM, fp32 output.
   razer_decode       RaZeR-A quantization of M x 5120 activations (M = 128),
-                     then the GEMM against RaZeR-W weights 17408 x 5120.
+                     then the GEMM against RaZeR-W weights 17408 x 5120;
+                     also reported at M = 1 and 16 (graph-timed).
 
 Inputs are resident in HBM before the timed region.  Prints one JSON line.
 Kernel times come from HIP events recorded on the stream the kernels run on
@@ -169,6 +170,38 @@ class RazerDecode:
                 "quant": "razer_a block16 auto-global bf16-in", "gemm": "razer_a x razer_w -> f32",
                 "M": self.M, "K": self.K, "N": [self.N]}
 
+    def small_m(self, ms=(1, 16)):
+        """The same step at decode batch sizes: RaZeR-A quantize of the first M
+        activation rows and the GEMM against the same weights, each timed over
+        20 launches captured in one HIP graph (these kernels run for tens of
+        microseconds, less than a launch from Python).  The GEMM streams the
+        weights once: % HBM is on those bytes."""
+        import torch
+        B = self.B
+        w_bytes = self.N * self.K // 2 + self.N * self.K // 16
+        res = []
+        for M in ms:
+            x = self.x[:M]
+            codes = torch.empty((M, self.K // 2), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((M, self.K // 16), dtype=torch.uint8, device="cuda")
+            g = torch.ones(1, dtype=torch.float32, device="cuda")
+            out = torch.empty((M, self.N), dtype=torch.float32, device="cuda")
+            t_q = graph_us(lambda: B.quantize(x, "razer_a", 16, "absmax", "auto", global_=g, codes=codes,
+                                              scales=scales))
+            # the same rows under NVFP4 abs-max, the plain rule the RaZeR-A time compares with
+            t_r1 = graph_us(lambda: B.quantize(x, "nvfp4", 16, "absmax", "auto", global_=g, codes=codes,
+                                               scales=scales))
+            B.quantize(x, "razer_a", 16, "absmax", "auto", global_=g, codes=codes, scales=scales)
+            t_g = graph_us(lambda: B.gemm("razer_a", codes, scales, g, "razer_w", self.wc, self.ws, self.wg,
+                                          self.sp, out=out))
+            gbs = w_bytes / (t_g * 1e-6) / 1e9
+            res.append({"M": M, "quantize_us": round(t_q, 2), "quantize_absmax_nvfp4_us": round(t_r1, 2),
+                        "gemm_us": round(t_g, 2),
+                        "gemm_weight_bytes": w_bytes, "gemm_GB/s": round(gbs, 1),
+                        "gemm_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "gemm_hbm_floor_us": round(w_bytes / (HBM_PEAK_GBS * 1e3), 2)})
+        return res
+
     def step(self, ev=None):
         B = self.B
         if ev: ev.mark("q0")
@@ -179,6 +212,30 @@ class RazerDecode:
 
 
 WORKLOADS = {"prefill": Prefill, "mxfp4_linear": MxLinear, "razer_decode": RazerDecode}
+
+
+def graph_us(fn, launches: int = 20, replays: int = 5) -> float:
+    """microseconds per call of fn, from `launches` calls captured in one HIP
+    graph and replayed, timed with HIP events on the replaying stream"""
+    import torch
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(launches):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (launches * replays)
 
 
 class Marks:
@@ -442,6 +499,9 @@ def main():
                   "frac": round(f / (t * 1e-3) / 1e12 / peak, 4)} for n, t, f in zip(wl.NS, g_ms, wl.gemm_flops)],
         "roofline": roofline,
     }
+    if isinstance(wl, RazerDecode):
+        log("[bench] decode batch sizes")
+        out["decode_small_m"] = wl.small_m()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl)

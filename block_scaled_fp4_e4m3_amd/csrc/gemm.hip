@@ -800,34 +800,37 @@ hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- small M
-// M <= 32 (decode shapes), NVFP4 family, K a multiple of 512.  Each wave owns
-// 32 output columns and all M rows as one 32 x 32 MFMA accumulator (rows past
-// M are computed from the clamped last row and never stored).  A, at most 32
-// rows, is decoded once per workgroup into LDS in fragment order, a window of
-// kSmWin 64-element chunks at a time.  Each wave streams its 32 weight rows
-// from global memory through a ring of kSmRing chunks in registers; one
-// 16-byte load per lane brings a ring turn's scales (4 blocks of each of 4
-// chunks of its row) a turn ahead, and each turn also loads one chunk of the
-// next window's A.  The decode and the K permutation are those of the tile
-// kernel.  The splits of K, whole windows each, add into a zero-filled FP32 C
-// with atomics.
+// M <= 128 (decode shapes), NVFP4 family, K a multiple of 64 windows.  Each
+// wave owns 32 output columns and all M rows as MR stacked 32 x 32 MFMA
+// accumulators (MR = 1, 2 or 4 row blocks; rows past M are computed from the
+// clamped last row and never stored).  A is decoded once per workgroup (4
+// waves for one block, 8 for more, so that decoding A stays a small share)
+// into LDS in fragment order, a window of WIN 64-element chunks at a time,
+// each wave taking a fixed share of the window's (chunk, row block) pieces.
+// Each wave streams its 32 weight rows from global memory through a ring of
+// two turns of kSmRing chunks in registers (a turn's refills are for the
+// chunks two turns on) and decodes each weight fragment once for its MR
+// MFMAs; one 16-byte load per lane brings a turn's scales (4 blocks of each
+// of 4 chunks of its row), and a window's first turn also loads the wave's
+// share of the next window's A.  The decode and the K
+// permutation are those of the tile kernel.  The splits of K, whole windows
+// each, add into a zero-filled FP32 C with atomics.
 //
 // No load is conditional: windows are full, the last window is peeled and its
 // last turn issues no refills.  Loads complete in issue order, and with the
 // same loads on every path the compiler's wait for a ring slot counts exactly
 // the loads issued after it, so the ring never drains.
-constexpr int kSmallM = 32;
+constexpr int kSmallM = 128;
 constexpr int kSmRing = 4;  // chunks per ring turn, one scale load each turn
-#ifndef FP4Q_SM_WIN
-#define FP4Q_SM_WIN 8
-#endif
-#ifndef FP4Q_SM_WGS_PER_CU
-#define FP4Q_SM_WGS_PER_CU 4
-#endif
-constexpr int kSmWin = FP4Q_SM_WIN;
-static_assert(kSmWin % kSmRing == 0 && kSmWin % 4 == 0, "a window is whole ring turns and wave rounds");
-constexpr int kSmTurns = kSmWin / kSmRing;  // ring turns per window = A chunks a wave decodes per window
-static_assert(kSmTurns == kSmWin / 4, "one A chunk per wave per turn");
+
+template <int MR>
+struct SmCfg {
+  static constexpr int WIN = 8;                  // chunks per A window (two turns): LDS of WIN x MR x 4 KiB
+  static constexpr int WAVES = MR == 1 ? 4 : 8;  // waves per workgroup: 32 WAVES output columns
+  static constexpr int TURNS = WIN / kSmRing;    // ring turns per window
+  static constexpr int FPW = WIN * MR / WAVES;   // A pieces (chunk x row block) a wave decodes per window
+  static_assert(TURNS == 2 && FPW * WAVES == WIN * MR, "two turns, even shares");
+};
 
 // buffer views of one operand for the rows [r0, r0 + 32)
 struct SmRows {
@@ -847,10 +850,11 @@ __device__ __forceinline__ SmRows sm_rows(const uint8_t* codes, const uint8_t* s
   return v;
 }
 
-// chunk kc of an A row: 32 codes and the scale bytes of the lane's two blocks
-__device__ __forceinline__ void sm_load_a(const SmRows& v, int64_t kc, int kh, uint4& c, uint32_t& sc) {
+// chunk kc of an A row: 32 codes and the 4 scale bytes of the chunk (the
+// lane's two blocks are the half kh of them)
+__device__ __forceinline__ void sm_load_a(const SmRows& v, int64_t kc, uint4& c, uint32_t& sc) {
   c = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(v.codes, v.voff_c, (int)(kc * 32), 0));
-  sc = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.voff_s + 2 * kh, (int)(kc * 4), 0);
+  sc = __builtin_amdgcn_raw_buffer_load_b32(v.scales, v.voff_s, (int)(kc * 4), 0);
 }
 
 // chunk kc of a W row: the lane's 32 codes
@@ -875,137 +879,197 @@ __device__ __forceinline__ void sm_decode(const uint4& c, uint32_t sc, uint32_t 
 }
 
 // chunks per split: whole windows, as even as that allows
-__host__ __device__ inline int64_t sm_split_len(int64_t nch, int64_t splits) {
+__host__ __device__ inline int64_t sm_split_len(int64_t nch, int64_t splits, int win) {
   const int64_t q = (nch + splits - 1) / splits;
-  return (q + kSmWin - 1) / kSmWin * kSmWin;
+  return (q + win - 1) / win * win;
 }
 
-template <int FA, int FW, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(GemmParams p) {
-  __shared__ __align__(16) half8 adec[kSmWin][4][64];
+template <int FA, int FW, bool OUT_BF16, int MR>
+__global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm_small_m_kernel(GemmParams p) {
+  using C = SmCfg<MR>;
+  constexpr int WIN = C::WIN, TURNS = C::TURNS, FPW = C::FPW;
+  __shared__ __align__(16) half8 adec[WIN][MR][4][64];
   const int split = (int)(blockIdx.x % (unsigned)p.splits);
   const int64_t slab = blockIdx.x / (unsigned)p.splits;
   // the wave index is uniform: read it into a scalar so that the buffer
   // views built from it stay in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
-  const int64_t n0 = slab * 128 + wave * 32;
+  const int64_t n0 = slab * (32 * C::WAVES) + wave * 32;
   const bool live = n0 < p.N;  // waves past N read row N - 1 and decode their share of A
-  const int64_t nch = p.K / 64, per = sm_split_len(nch, p.splits);
+  const int64_t nch = p.K / 64, per = sm_split_len(nch, p.splits, WIN);
   const int64_t cb = split * per, ce = min(nch, cb + per);  // cb < ce: every split is used
   const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
   const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
-  const SmRows av = sm_rows(p.a_codes, p.a_scales, 0, p.M, p.K, r32, kh);
+  // the wave's A pieces: piece t is chunk (wave + WAVES t) % WIN of a window,
+  // row block (wave + WAVES t) / WIN
+  SmRows av[FPW];
+  int pc[FPW], pb[FPW];
+  static_for<0, FPW>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const int f = wave + C::WAVES * t;
+    pc[t] = f % WIN;
+    pb[t] = f / WIN;
+    av[t] = sm_rows(p.a_codes, p.a_scales, min((int64_t)(32 * pb[t]), p.M - 1), p.M, p.K, r32, kh);
+  });
   const SmRows wv = sm_rows(p.w_codes, p.w_scales, live ? n0 : p.N - 1, p.N, p.K, r32, kh);
 
-  f32x16 acc = {};
-  uint4 rc[kSmRing], ca[kSmTurns], scur, snext;
-  uint32_t sa[kSmTurns];
-  static_for<0, kSmTurns>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    sm_load_a(av, cb + wave + 4 * j, kh, ca[j], sa[j]);
+  f32x16 acc[MR];
+  static_for<0, MR>([&](auto bc) { acc[decltype(bc)::value] = f32x16{}; });
+  // ring: turn J of every window holds its chunks in rc[J] and their scales
+  // in sc[J]; per >= WIN, so the first two turns are inside the split
+  uint4 rc[TURNS][kSmRing], sc[TURNS], ca[FPW];
+  uint32_t sa[FPW];
+  static_for<0, FPW>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    sm_load_a(av[t], cb + pc[t], ca[t], sa[t]);
   });
   __builtin_amdgcn_sched_barrier(0);  // A first, then the ring in slot order
-  scur = sm_scales4(wv, cb);
-  static_for<0, kSmRing>([&](auto uc) {
-    constexpr int u = decltype(uc)::value;
-    rc[u] = sm_codes(wv, cb + u);
+  static_for<0, TURNS>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    static_for<0, kSmRing>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      rc[J][u] = sm_codes(wv, cb + kSmRing * J + u);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    sc[J] = sm_scales4(wv, cb + kSmRing * J);
     __builtin_amdgcn_sched_barrier(0);
   });
-  snext = sm_scales4(wv, min(cb + kSmRing, ce - kSmRing));
-  __builtin_amdgcn_sched_barrier(0);
 
-  // turn J of the window at wb: chunks g0 .. g0 + 3
+  // turn J of the window at wb: chunks g0 .. g0 + 3; with `refill`, loads
+  // the same turn of the next window
   auto turn = [&](int64_t wb, auto jc, auto refill, auto next_a) {
     constexpr int J = decltype(jc)::value;
+    constexpr bool RF = decltype(refill)::value;
     const int64_t g0 = wb + kSmRing * J;
-    if constexpr (decltype(next_a)::value) {
-      sm_load_a(av, wb + kSmWin + wave + 4 * J, kh, ca[J], sa[J]);
+    if constexpr (decltype(next_a)::value && J == 0) {  // a whole window ahead
+      static_for<0, FPW>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        sm_load_a(av[t], wb + WIN + pc[t], ca[t], sa[t]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t sw[kSmRing];
+    static_for<0, kSmRing>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      sw[u] = u4_get(sc[J], u) >> (16 * kh);
+      asm volatile("" : "+v"(sw[u]));  // computed here, not sunk into the steps past the reload
+    });
+    if constexpr (RF) {
+      // the words are out before the reload: sc[J] keeps its registers
+      __builtin_amdgcn_sched_barrier(0);
+      sc[J] = sm_scales4(wv, g0 + WIN);
       __builtin_amdgcn_sched_barrier(0);
     }
     static_for<0, kSmRing>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      const uint32_t sw = u4_get(scur, u) >> (16 * kh);
       // decode the slot, then refill it: the refill's registers are then free
       // and stay the slot's own, with no copies around the loop
-      half8 b[4];
-      if (live) sm_decode<FW>(rc[u], sw, sp_lo, sp_hi, b);
+      half8 w[4];
+      if (live) sm_decode<FW>(rc[J][u], sw[u], sp_lo, sp_hi, w);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(refill)::value) rc[u] = sm_codes(wv, g0 + kSmRing + u);
+      if constexpr (RF) rc[J][u] = sm_codes(wv, g0 + WIN + u);
       __builtin_amdgcn_sched_barrier(0);
       if (live) {
         static_for<0, 4>([&](auto ic) {
           constexpr int I = decltype(ic)::value;
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(adec[kSmRing * J + u][I][lane], b[I], acc, 0, 0, 0);
+          static_for<0, MR>([&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(adec[kSmRing * J + u][b][I][lane], w[I], acc[b], 0, 0, 0);
+          });
         });
       }
     });
-    if constexpr (decltype(refill)::value) {
-      scur = snext;
-      snext = sm_scales4(wv, min(g0 + 2 * kSmRing, ce - kSmRing));
-    }
   };
   auto window = [&](int64_t wb, auto lastw) {
     constexpr bool LW = decltype(lastw)::value;
     lds_barrier();  // the previous window's fragments have been read
-    static_for<0, kSmTurns>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
+    static_for<0, FPW>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       half8 d[4];
-      sm_decode<FA>(ca[j], sa[j], sp_lo, sp_hi, d);
+      sm_decode<FA>(ca[t], sa[t] >> (16 * kh), sp_lo, sp_hi, d);
       static_for<0, 4>([&](auto ic) {
         constexpr int I = decltype(ic)::value;
-        adec[wave + 4 * j][I][lane] = d[I];
+        adec[pc[t]][pb[t]][I][lane] = d[I];
       });
     });
     lds_barrier();
-    static_for<0, kSmTurns>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      turn(wb, jc, std::integral_constant<bool, !(LW && j == kSmTurns - 1)>{}, std::integral_constant<bool, !LW>{});
+    static_for<0, TURNS>([&](auto jc) {
+      turn(wb, jc, std::integral_constant<bool, !LW>{}, std::integral_constant<bool, !LW>{});
     });
   };
   int64_t wb = cb;
-  for (; wb + kSmWin < ce; wb += kSmWin) window(wb, std::false_type{});
+  for (; wb + WIN < ce; wb += WIN) window(wb, std::false_type{});
   window(wb, std::true_type{});
   if (!live) return;
 
   const float gg = (p.a_global ? *p.a_global : 1.0f) * (p.w_global ? *p.w_global : 1.0f);
   const int64_t col = n0 + r32;
   if (col >= p.N) return;
+  static_for<0, MR>([&](auto bc) {
+    constexpr int b = decltype(bc)::value;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t row = (r / 4) * 8 + kh * 4 + (r % 4);
-    if (row >= p.M) continue;
-    const float v = gg * acc[r];
-    if constexpr (OUT_BF16) {
-      uint32_t u = __float_as_uint(v);
-      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
-      ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
-    } else if (p.splits > 1) {
-      atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
-    } else {
-      ((float*)p.c)[row * p.ldc + col] = v;
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = 32 * b + (r / 4) * 8 + kh * 4 + (r % 4);
+      if (row >= p.M) continue;
+      const float v = gg * acc[b][r];
+      if constexpr (OUT_BF16) {
+        uint32_t u = __float_as_uint(v);
+        u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+        ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
+      } else if (p.splits > 1) {
+        atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
+      } else {
+        ((float*)p.c)[row * p.ldc + col] = v;
+      }
     }
-  }
+  });
 }
 
-// the small-M kernel takes K a multiple of 64 kSmWin (whole windows) and
-// operands aligned for its 16-byte code and scale loads
+int sm_blocks(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
+int sm_win(int mr) { return mr == 1 ? SmCfg<1>::WIN : mr == 2 ? SmCfg<2>::WIN : SmCfg<4>::WIN; }
+
+// the small-M kernel takes K a multiple of 64 windows and operands aligned
+// for its 16-byte code and scale loads
 bool small_m_fits(const GemmParams& p) {
   const uintptr_t a = (uintptr_t)p.a_codes | (uintptr_t)p.w_codes | (uintptr_t)p.a_scales | (uintptr_t)p.w_scales;
-  return p.M <= kSmallM && p.K % (64 * kSmWin) == 0 && (a & 15u) == 0;
+  return p.M <= kSmallM && p.K % (64 * sm_win(sm_blocks(p.M))) == 0 && (a & 15u) == 0;
 }
 
-template <int FA, int FW>
-hipError_t launch_small_m(const GemmParams& p0, hipStream_t s) {
+// FP32 output splits K: the split count minimises an estimate of the time,
+// rounds of resident workgroups x chunks per split plus the FP32 atomics the
+// splits add (measured on MI355X: about 1.1 us per chunk and round, 3.2 us
+// per million atomics)
+int64_t sm_choose_splits(int64_t M, int64_t N, int64_t nch, int64_t slabs, int64_t slots, int win) {
+  int64_t best = 1;
+  double best_t = 1e300;
+  for (int64_t sp = 1; sp <= nch / win; ++sp) {
+    const int64_t len = sm_split_len(nch, sp, win), used = (nch + len - 1) / len;
+    if (used != sp) continue;
+    const double rounds = (double)((slabs * sp + slots - 1) / slots);
+    const double t = rounds * (double)len * 1.1 + (sp > 1 ? 3.2e-6 * (double)(sp * M * N) : 0.0);
+    if (t < best_t) { best_t = t; best = sp; }
+  }
+  return best;
+}
+
+template <int FA, int FW, int MR>
+hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s) {
+  constexpr int WIN = SmCfg<MR>::WIN, WAVES = SmCfg<MR>::WAVES;
   GemmParams p = p0;
-  const int64_t slabs = (p.N + 127) / 128, nch = p.K / 64;
-  // FP32 output: splits of K for about FP4Q_SM_WGS_PER_CU workgroups per CU
+  const int64_t slabs = (p.N + 32 * WAVES - 1) / (32 * WAVES), nch = p.K / 64;
   int64_t sp = 1;
   if (!p.c_bf16) {
-    sp = (FP4Q_SM_WGS_PER_CU * (int64_t)device_cus() + slabs - 1) / slabs;
-    if (sp > nch / kSmWin) sp = nch / kSmWin;
-    if (sp < 1) sp = 1;
-    sp = (nch + sm_split_len(nch, sp) - 1) / sm_split_len(nch, sp);  // splits in use
+    // resident workgroups per CU, as the runtime reports them for this kernel
+    static int per_cu = 0;
+    if (per_cu == 0) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR>, 64 * WAVES, 0)
+          != hipSuccess || nb < 1)
+        nb = 1;
+      per_cu = nb;
+    }
+    sp = sm_choose_splits(p.M, p.N, nch, slabs, (int64_t)per_cu * device_cus(), WIN);
   }
   p.splits = (int)sp;
   if (sp > 1) {
@@ -1013,9 +1077,19 @@ hipError_t launch_small_m(const GemmParams& p0, hipStream_t s) {
     hipLaunchKernelGGL(zero_c_kernel, dim3(gx, gy), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
   }
   const unsigned grid = (unsigned)(slabs * sp);
-  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true>), dim3(grid), dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false>), dim3(grid), dim3(kThreads), 0, s, p);
+  const unsigned threads = 64 * WAVES;
+  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR>), dim3(grid), dim3(threads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR>), dim3(grid), dim3(threads), 0, s, p);
   return hipGetLastError();
+}
+
+template <int FA, int FW>
+hipError_t launch_small_m(const GemmParams& p, hipStream_t s) {
+  switch (sm_blocks(p.M)) {
+    case 1: return launch_small_m_mr<FA, FW, 1>(p, s);
+    case 2: return launch_small_m_mr<FA, FW, 2>(p, s);
+    default: return launch_small_m_mr<FA, FW, 4>(p, s);
+  }
 }
 
 template <int FA, int FW>

@@ -70,12 +70,14 @@ def test_gemm_small(B, fa, fw, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
-# decode shapes (M <= 32): several K splits and A windows (K a multiple of
-# 512), the smallest K, waves past N, and K that are not multiples of 512
-# (taken by the tile kernel)
+# decode shapes (M <= 128, in one, two or four row blocks of 32): several K
+# splits and A windows (K a multiple of 512, or of 256 for four blocks), the
+# smallest K, waves past N, and K the small-M kernel does not take (the tile
+# kernel's)
 @pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w"), ("nvfp4", "razer_a")])
 @pytest.mark.parametrize("M,N,K", [(5, 200, 2560), (32, 129, 4096), (1, 384, 4096), (2, 70, 512), (3, 64, 1040),
-                                   (9, 150, 2080)])
+                                   (9, 150, 2080), (40, 200, 2560), (64, 300, 1536), (70, 100, 2304),
+                                   (128, 64, 1024), (100, 129, 2048)])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_gemm_decode_shapes(B, fa, fw, M, N, K, out_dtype):
     a = datagen.student_t((M, K), 700 + M, 4.0)
