@@ -78,9 +78,10 @@ __device__ __forceinline__ double sf_val(int k) {
 }
 
 // E2M1 magnitudes and the midpoints between neighbours
-__constant__ float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+// (compile-time arrays, indexed with constants only: literals, no memory loads)
+constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
 constexpr double kMidD[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-__constant__ float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+constexpr float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
 
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
@@ -106,6 +107,7 @@ template <> struct Tables<MXFP4> { uint32_t dummy; };
 __device__ __forceinline__ void special_bounds(float av, float& lo, float& hi, bool& open_hi) {
   float below = 0.f, above = 0.f;
   open_hi = true;
+#pragma unroll
   for (int m = 0; m < 8; ++m) {
     if (kMag[m] < av) below = kMag[m];
     if (kMag[m] > av && open_hi) { above = kMag[m]; open_hi = false; }
@@ -121,11 +123,14 @@ __device__ void build_tables(Tables<FMT>& T, float g, const float* special) {
     constexpr int KN = Tables<FMT>::KN;
     constexpr int NSP = FmtTraits<FMT>::NSP;
     const double gd = (double)g;
-    for (int i = threadIdx.x; i < KN * 8; i += blockDim.x) {
-      int k = i >> 3, j = i & 7;
-      uint32_t v = 0x7F800000u;  // never passed by a finite |x|
-      if (k > 0 && j < 7) v = thr_bits((double)kMid[j] * sf_val<SF>(k) * gd, (j & 1) != 0);
-      T.elt[k][j] = v;
+    for (int k = threadIdx.x; k < KN; k += blockDim.x) {
+      const double sg = sf_val<SF>(k) * gd;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t v = 0x7F800000u;  // never passed by a finite |x|
+        if (k > 0 && j < 7) v = thr_bits(kMidD[j] * sg, (j & 1) != 0);
+        T.elt[k][j] = v;
+      }
     }
     for (int i = threadIdx.x; i < 2 * KN; i += blockDim.x) {
       int k = i % KN, which = i / KN;
@@ -885,9 +890,11 @@ hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   constexpr int L = (B == 4) ? 4 : 8;
   const int64_t chunks = p.rows * (p.cols / L);
   int grid = grid_for(chunks);
-  // kernels that build LDS tables per workgroup: at least 8 chunks per thread
+  // kernels that build LDS tables per workgroup: a few chunks per thread
+  // (2 for small tensors, where the grid is short of the CUs anyway, 4 above)
   if (FMT == RAZER_A || FMT == RAZER_W || RULE == BRUTE) {
-    const int64_t cap = (chunks + 256 * 8 - 1) / (256 * 8);
+    const int64_t per = chunks <= 65536 ? 2 : 4;
+    const int64_t cap = (chunks + kThreads * per - 1) / (kThreads * per);
     if (grid > cap) grid = (int)(cap < 1 ? 1 : cap);
   }
   // the brute-force search is compute-bound: one addressing variant suffices
