@@ -142,7 +142,7 @@ class RazerDecode:
     name = "razer_decode"
     M, K, N = 128, 5120, 17408
     compute_dtype = "f16"
-    gemm_kernel = "gemm_tile_kernel"
+    gemm_kernel = "gemm_small_m_kernel"
     quant_kernel = "quantize_kernel"
 
     def __init__(self, B, M=128):
