@@ -87,7 +87,7 @@ template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
 template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0, KMAX = 126, NSP = 2; };
 template <> struct FmtTraits<RAZER_W> { static constexpr int SF = 1, KMAX = 63,  NSP = 4; };
-template <> struct FmtTraits<MXFP4>   { static constexpr int SF = 2, KMAX = 0,   NSP = 0; };
+template <> struct FmtTraits<MXFP4>   { static constexpr int SF = 2; };
 
 // LDS tables, built once per workgroup for the launch's global scale g
 template <int FMT>
