@@ -203,6 +203,17 @@ __device__ __forceinline__ int rtn_mag(uint32_t xb, const uint32_t t[7]) {
   return (c2 ? 4 : 0) | (c1 ? 2 : 0) | (c0 ? 1 : 0);
 }
 
+// the same decision against thresholds held in scalars: a kernel whose
+// threshold array would be indexed through selected addresses gets the array
+// placed in LDS, and that alone costs its launches about 12 us here
+__device__ __forceinline__ int rtn_mag_v(uint32_t xb, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3,
+                                         uint32_t t4, uint32_t t5, uint32_t t6) {
+  const bool c2 = xb > t3;
+  const bool c1 = xb > (c2 ? t5 : t1);
+  const bool c0 = xb > (c2 ? (c1 ? t6 : t4) : (c1 ? t2 : t0));
+  return (c2 ? 4 : 0) | (c1 ? 2 : 0) | (c0 ? 1 : 0);
+}
+
 template <int L>
 struct Chunk {
   float x[L];
@@ -219,7 +230,27 @@ template <int L, bool BF16>
 struct Raw {
   static constexpr int W = BF16 ? L / 2 : L;  // 32-bit words
   uint32_t w[W];
+  float t[L];  // the chunk's channel scales, when loaded with the chunk
 };
+
+// buffer view of the channel scales; with none, a view of no bytes, whose
+// reads return zeros without touching memory
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chan_view(const QuantParams& p) {
+  const bool on = p.chan_scale != nullptr;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p.chan_scale, (short)0, on ? (int)(p.cols * 4) : 0,
+                                           (int)0x00020000);
+}
+
+// the chunk's channel scales, issued with the chunk's load so that one wait
+// covers both
+template <int L, bool BF16>
+__device__ __forceinline__ void load_t(__amdgpu_buffer_rsrc_t tv, int64_t j0, Raw<L, BF16>& raw) {
+#pragma unroll
+  for (int i = 0; i < L; i += 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(tv, (int)((j0 + i) * 4), 0, 0);
+    raw.t[i] = bitsf(v[0]); raw.t[i + 1] = bitsf(v[1]); raw.t[i + 2] = bitsf(v[2]); raw.t[i + 3] = bitsf(v[3]);
+  }
+}
 
 template <int L, bool BF16>
 __device__ __forceinline__ void load_raw(const QuantParams& p, int64_t r, int64_t j0, Raw<L, BF16>& raw) {
@@ -244,7 +275,7 @@ __device__ __forceinline__ void load_raw(const QuantParams& p, int64_t r, int64_
 
 // widen a raw chunk, apply the channel scale and the size-32 block-Hadamard
 // (lanes of a 32-group are adjacent)
-template <int L, bool BF16>
+template <int L, bool BF16, bool PRE_T = false>
 __device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, const Raw<L, BF16>& raw, float* x,
                                              bool chan, bool had) {
   if constexpr (BF16) {
@@ -258,10 +289,15 @@ __device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, c
     for (int i = 0; i < L; ++i) x[i] = bitsf(raw.w[i]);
   }
   if (chan) {
+    if constexpr (PRE_T) {
 #pragma unroll
-    for (int i = 0; i < L; i += 4) {
-      float4 t = *(const float4*)(p.chan_scale + j0 + i);
-      x[i] = x[i] * t.x; x[i + 1] = x[i + 1] * t.y; x[i + 2] = x[i + 2] * t.z; x[i + 3] = x[i + 3] * t.w;
+      for (int i = 0; i < L; ++i) x[i] = x[i] * raw.t[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; i += 4) {
+        float4 t = *(const float4*)(p.chan_scale + j0 + i);
+        x[i] = x[i] * t.x; x[i + 1] = x[i + 1] * t.y; x[i + 2] = x[i + 2] * t.z; x[i + 3] = x[i + 3] * t.w;
+      }
     }
   }
   if (had) {
@@ -313,6 +349,20 @@ __device__ __forceinline__ uint32_t encode_plain(const float* x, const uint32_t 
     uint32_t b = fbits(x[i]);
     int m = rtn_mag(b & 0x7FFFFFFFu, t);
     uint32_t c = m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u;
+    packed |= c << (4 * i);
+  }
+  return packed;
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t encode_plain_v(const float* x, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3,
+                                                   uint32_t t4, uint32_t t5, uint32_t t6) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const uint32_t b = fbits(x[i]);
+    const int m = rtn_mag_v(b & 0x7FFFFFFFu, t0, t1, t2, t3, t4, t5, t6);
+    const uint32_t c = m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u;
     packed |= c << (4 * i);
   }
   return packed;
@@ -581,7 +631,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   // chunk c = r * cpr + cj; the division happens once, then (r, cj) advance.
   // Each iteration issues the loads of U chunks (c, c + stride, ...) before
   // working on the first, to keep enough bytes in flight per CU.
-  constexpr int U = (FMT == MXFP4) ? 1 : 2;
+  constexpr int U = (FMT == MXFP4 && CONTIG) ? 1 : 2;
+  const __amdgpu_buffer_rsrc_t tv = chan_view(p);
   int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   int64_t r0 = CONTIG ? 0 : c / cpr, cj0 = CONTIG ? c : c % cpr;
   const int64_t sr = CONTIG ? 0 : stride / cpr, sc = CONTIG ? stride : stride % cpr;
@@ -608,13 +659,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         }
       }
       load_raw<L, BF16>(p, ru[u], cu[u] * L, raw[u]);
+      if constexpr (!CONTIG) load_t<L, BF16>(tv, cu[u] * L, raw[u]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all of the iteration's loads before the first wait
 #pragma unroll
     for (int u = 0; u < U; ++u) {
     const bool valid = vu[u];
     const int64_t r = ru[u], cj = cu[u];
     float x[L];
-    finish_chunk<L, BF16>(p, cj * L, raw[u], x, chan, had);
+    finish_chunk<L, BF16, !CONTIG>(p, cj * L, raw[u], x, chan, had);
 
     uint32_t amax = 0;
 #pragma unroll
@@ -643,13 +696,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         });
         packed = clear_neg_zero(packed);
       } else {
-        uint32_t t[7];
-#pragma unroll
-        for (int j = 0; j < 7; ++j) {
-          uint32_t b = fbits(ldexpf(kMid[j], E));   // exact
-          t[j] = (j & 1) ? b - 1 : b;
-        }
-        packed = encode_plain<L>(x, t);
+        // thresholds 2^E x midpoints (exact), as bit patterns: strict > for
+        // the even ones, >= (one below) for the odd ones (ties to even)
+        const uint32_t t0 = fbits(ldexpf(kMid[0], E)), t1 = fbits(ldexpf(kMid[1], E)) - 1u;
+        const uint32_t t2 = fbits(ldexpf(kMid[2], E)), t3 = fbits(ldexpf(kMid[3], E)) - 1u;
+        const uint32_t t4 = fbits(ldexpf(kMid[4], E)), t5 = fbits(ldexpf(kMid[5], E)) - 1u;
+        const uint32_t t6 = fbits(ldexpf(kMid[6], E));
+        packed = encode_plain_v<L>(x, t0, t1, t2, t3, t4, t5, t6);
       }
       sbyte = (uint8_t)(E + 127);
     } else if constexpr (FMT == NVFP4) {
