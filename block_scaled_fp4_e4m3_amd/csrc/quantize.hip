@@ -38,8 +38,8 @@ __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); 
 // other distances through the LDS crossbar
 template <int D>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-  else if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+  else if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
   else return (uint32_t)__shfl_xor((int)v, D);
 }
 __device__ __forceinline__ float lane_xor_f(float v, int d) {
