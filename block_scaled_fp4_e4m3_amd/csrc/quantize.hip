@@ -85,7 +85,7 @@ constexpr float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
 
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
-template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0, KMAX = 126, NSP = 2; };
+template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0; };
 template <> struct FmtTraits<RAZER_W> { static constexpr int SF = 1, KMAX = 63,  NSP = 4; };
 template <> struct FmtTraits<MXFP4>   { static constexpr int SF = 2; };
 
@@ -601,9 +601,10 @@ template <int FMT, int B, int RULE, bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   constexpr int L = (B == 4) ? 4 : 8;
   constexpr int LPB = B / L;  // lanes per block
-  // LDS tables serve RaZeR and the brute-force search; NVFP4 abs-max and
-  // 4-over-6 and MXFP4 form their rare exact decisions on the fly
-  constexpr bool TABLES = (FMT == RAZER_A || FMT == RAZER_W || RULE == BRUTE);
+  // LDS tables serve RaZeR-W (E3M3 scales) and the brute-force search;
+  // NVFP4 (abs-max, 4-over-6), RaZeR-A and MXFP4 form their rare exact
+  // decisions on the fly
+  constexpr bool TABLES = (FMT == RAZER_W || RULE == BRUTE);
   __shared__ Tables<TABLES ? FMT : MXFP4> T;
   const float g = p.global ? *p.global : 1.0f;
   if constexpr (TABLES) {
@@ -748,6 +749,50 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
           if (e4 < e6) { packed = pk4; sbyte = (uint8_t)k4; }
         }
       }
+    } else if constexpr (FMT == RAZER_A) {
+      // RaZeR-A: the abs-max E4M3 scale and element codes of NVFP4 (the same
+      // rule: nearest E4M3 to amax / (6 g), ties to even), then the special
+      // value +5 or -5 with the lower block error (ties keep +5).  A special
+      // takes the elements of its sign strictly inside (4.5, 5.5) s g, the
+      // midpoints to its neighbours 4 and 6; both bounds are exact products in
+      // binary64, rounded down (strict >) and up (strict <) to FP32 patterns.
+      const bool finite = amax < 0x7F800000u;
+      int k;
+      if (wave_all(fast_scale && finite)) {
+        typedef short s2v __attribute__((ext_vector_type(2)));
+        const float a = bitsf(amax);
+        const s2v z = {0, 0};
+        const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * lo6, a, 1.0f, false);
+        k = e4m3_from_low((uint16_t)clo[0] & 0xFFu, a, 6.0f, g);
+      } else {
+        k = select_e4m3_exact(bitsf(amax), inv6, 6.0 * (double)g);
+      }
+      if (p.prevent_zero && k == 0) k = 1;
+      const float s = e4m3_f32(k);
+      const uint32_t base = encode_nv<L, LPB>(x, k, s, g, finite);
+      const double sg = (double)s * (double)g;
+      const uint32_t lo = thr_bits(4.5 * sg, false), hi = ru_bits(5.5 * sg);
+      float best = 0.f;
+      int bestp = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t vsign = q ? 0x80000000u : 0u;
+        uint32_t pk = base;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+          const uint32_t b = fbits(x[i]), xb = b & 0x7FFFFFFFu;
+          const bool sp = ((b & 0x80000000u) == vsign) && xb > lo && xb < hi;
+          pk = sp ? ((pk & ~(0xFu << (4 * i))) | (8u << (4 * i))) : pk;
+        }
+        const float v = q ? -5.0f : 5.0f;
+        const float e = group_sum<LPB>(lane_sse<L>(x, pk, s, g, true, v * s));
+        if (q == 0 || e < best) { best = e; bestp = q; packed = pk; }
+      }
+      if (k == 0) {
+        packed = 0;
+        bestp = 0;
+      }
+      sbyte = (uint8_t)((bestp << 7) | k);
     } else {
       // RaZeR: abs-max scale (E4M3 for activations, E3M3 for weights), then
       // the special value with the lowest block error (ties keep the first)
@@ -945,7 +990,7 @@ hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   int grid = grid_for(chunks);
   // kernels that build LDS tables per workgroup: a few chunks per thread
   // (2 for small tensors, where the grid is short of the CUs anyway, 4 above)
-  if (FMT == RAZER_A || FMT == RAZER_W || RULE == BRUTE) {
+  if (FMT == RAZER_W || RULE == BRUTE) {
     const int64_t per = chunks <= 65536 ? 2 : 4;
     const int64_t cap = (chunks + kThreads * per - 1) / (kThreads * per);
     if (grid > cap) grid = (int)(cap < 1 ? 1 : cap);
