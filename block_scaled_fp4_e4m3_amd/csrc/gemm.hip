@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp4q {
 namespace {
 
@@ -756,14 +758,24 @@ __global__ __launch_bounds__(256) void zero_c_kernel(float* c, int64_t M, int64_
   }
 }
 
+// per-device caches of launch facts (0: not yet known); every thread that
+// fills an entry writes the same value, so relaxed atomics suffice
+constexpr int kMaxDevices = 64;
+
+int current_device() {
+  int dev = 0;
+  return (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) ? dev : -1;
+}
+
 int device_cus() {
-  static int cus = 0;
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device();
+  int cus = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+    int n = 0;
+    cus = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) == hipSuccess && n > 0)
+              ? n : 256;
+    if (dev >= 0) cache[dev].store(cus, std::memory_order_relaxed);
   }
   return cus;
 }
@@ -1061,13 +1073,16 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s) {
   int64_t sp = 1;
   if (!p.c_bf16) {
     // resident workgroups per CU, as the runtime reports them for this kernel
-    static int per_cu = 0;
+    static std::atomic<int> cache[kMaxDevices];
+    const int dev = current_device();
+    int per_cu = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
     if (per_cu == 0) {
       int nb = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR>, 64 * WAVES, 0)
           != hipSuccess || nb < 1)
         nb = 1;
       per_cu = nb;
+      if (dev >= 0) cache[dev].store(per_cu, std::memory_order_relaxed);
     }
     sp = sm_choose_splits(p.M, p.N, nch, slabs, (int64_t)per_cu * device_cus(), WIN);
   }
