@@ -721,6 +721,40 @@ void gemm_tile_kernel(GemmParams p) {
   const int r32 = lane & 31, kh = lane >> 5;
   const int64_t row0 = m0 + wm * 128, col0 = n0 + wn * 128;
   const bool inside = row0 + 128 <= p.M && col0 + 128 <= p.N;
+  constexpr int ES = OUT_BF16 ? 2 : 4;  // output element bytes
+  const int64_t pitch = p.ldc * ES;
+  if (inside && (OUT_BF16 || p.splits == 1) && pitch < (int64_t)1 << 23) {
+    // a whole wave tile and plain stores: a buffer view of the wave tile's
+    // first element, the lane's column and row quad in the vector offset, the
+    // rest of each element's offset (row within the tile, column block) scalar
+    // and immediate; 128 rows x pitch < 2^30 bytes keeps every offset in range
+    const uint64_t bp = (uint64_t)((uint8_t*)p.c + (row0 * p.ldc + col0) * ES);
+    // uniform; each half back to unsigned before widening (the builtin returns int)
+    const uint32_t bp_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32));
+    const uint32_t bp_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+    uint8_t* base = (uint8_t*)(((uint64_t)bp_hi << 32) | (uint64_t)bp_lo);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, -1, (int)kRsrcWord3);
+    const int ld = (int)pitch;
+    const int voff = kh * 4 * ld + r32 * ES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int soff = (32 * i + (r / 4) * 8 + (r % 4)) * ld;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = gg * acc[i][j][r];
+          if constexpr (OUT_BF16) {
+            uint32_t u = __float_as_uint(v);
+            u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)u, rc, voff + 32 * j * ES, soff, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, voff + 32 * j * ES, soff, 0);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll

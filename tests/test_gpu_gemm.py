@@ -92,6 +92,54 @@ def test_gemm_decode_shapes(B, fa, fw, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
+def _high_low_word_offset(lo, nbytes):
+    """Byte offset (a multiple of 256) from an address whose low 32 bits are
+    `lo` to the first one whose low 32 bits lie in [2^31, 2^32 - nbytes]."""
+    if 2**31 <= lo and lo + nbytes <= 2**32:
+        return 0
+    return ((2**32 + 2**31 - lo) % 2**32 + 255) & ~255
+
+
+def test_high_low_word_offset():
+    for lo in (0, 256, 2**31 - 512, 2**31, 2**32 - 4096, 2**32 - 256):
+        off = _high_low_word_offset(lo, 4096)
+        assert off % 256 == 0 and off <= 2**31 + 4096
+        assert 2**31 <= (lo + off) % 2**32 <= 2**32 - 4096
+
+
+# C where the low 32 bits of every tile's address have bit 31 set: the
+# epilogue forms 64-bit addresses from two 32-bit halves.  K = 128 is one
+# stage, so FP32 output runs without K splits; 300 x 260 has whole wave tiles
+# and ragged ones.
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("mxfp4", "mxfp4")])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_output_address_low_word_above_2g(B, fa, fw, out_dtype):
+    import torch
+    M, N, K = 300, 260, 128
+    a = datagen.student_t((M, K), 910, 4.0)
+    w = datagen.normal((N, K), 911, 0.02)
+    ca, sa, ga = oquant(a, fa)
+    cw, sw, gw = oquant(w, fw)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, None, M, N, K)
+    dt, es = (torch.float32, 4) if out_dtype == "f32" else (torch.bfloat16, 2)
+    ld = -(-N // (16 // es)) * (16 // es)
+    nbytes = M * ld * es
+    big = torch.empty(2**31 + 2**22, dtype=torch.uint8, device="cuda")
+    off = _high_low_word_offset(big.data_ptr() % 2**32, nbytes)
+    assert off + nbytes <= big.numel() and (big.data_ptr() + off) % 2**32 >= 2**31
+    out = big[off:off + nbytes].view(dt).view(M, ld)
+    c = out[:, :N]
+    case(f"gemm {fa}x{fw} {M}x{N}x{K} {out_dtype} at low word {(big.data_ptr() + off) % 2**32:#x}")
+    B.gemm(fa, dev(ca), dev(sa), scalar_dev(ga), fw, dev(cw), dev(sw), scalar_dev(gw), None, out=c)
+    torch.cuda.synchronize()
+    got = host(c)
+    if out_dtype != "f32":
+        got = datagen.bf16_bits_to_f32(got)
+    del out, c, big
+    tol = TOL if out_dtype == "f32" else 8e-3
+    assert rel_fro(got, ref) <= tol
+
+
 @pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("mxfp4", "mxfp4"), ("razer_a", "razer_w")])
 def test_gemm_exact_regime_bitwise(B, fa, fw):
     # g = 1, every block scale 1 (E4M3 code 56, E8M0 127, E3M3 code 24), K <= 256:
