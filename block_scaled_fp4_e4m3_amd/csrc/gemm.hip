@@ -688,13 +688,232 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
   }
 }
 
+// ---------------------------------------------------------------- MXFP4 K loop, LDS-DMA staging
+// For MXFP4 with whole stages (K % 128 == 0), 16-byte aligned code rows and
+// word-aligned scale rows.  Global loads write LDS directly (buffer_load ...
+// lds: lane l of a load lands at 16 l, or 4 l, bytes past the wave's LDS
+// address), so staging needs no registers and no LDS store instructions, and
+// a ring of four stage buffers lets the loads of stage s + 3 start at the top
+// of stage s.
+//   codes: 1 KiB block q holds rows 16 q .. 16 q + 15 (the stage's 64 bytes
+//     of each), row 16 q + r16's chunk c at slot 64 q + 4 r16 + (c ^ ((r16 >>
+//     2) & 3)).  Load unit q (one wave instruction) fills block q: lane l
+//     fetches row 16 q + l / 4, chunk (l % 4) ^ ((l / 16) % 4), so each four
+//     lanes read one row's 64 bytes.  A fragment read of tile g, chunk kc
+//     (lane (r32, kh): row 32 g + r32, chunk 2 kc + kh) covers blocks 2 g and
+//     2 g + 1, and any 16 consecutive lanes hit 16 distinct slots mod 16.
+//   scales: the stage's four E8M0 bytes of each row as one dword (row r at
+//     4 r); lane (r32, kh) shifts its row's dword right by 8 kh, so that the
+//     MFMA's byte select 2 kc picks block 2 kc + kh.
+constexpr int kDlCodes = BM * KB;                  // 16 KiB per operand
+constexpr int kDlBuf = 2 * kDlCodes + 2 * BM * 4;  // 34 KiB
+constexpr int kDlNbuf = 4;
+constexpr int kDlLds = kDlNbuf * kDlBuf;           // 136 KiB
+constexpr int kDlLoads = 10;                       // load instructions per wave per stage
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup barrier of the LDS-DMA ring: this wave's LDS reads complete and
+// at most N of its loads still in flight (the newest), then all waves meet.
+// A release fence would also wait for every load in flight (they write LDS),
+// so the wait is explicit; the empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void dl_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt N, lgkmcnt 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct DlLoader {
+  __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+  uint32_t a_off[4], w_off[4];  // this lane's row and chunk offsets in its 4 A and 4 W units
+  uint32_t sa_off, sw_off;      // this thread's scale row
+  int wv;                       // wave index (uniform)
+
+  __device__ void init(const GemmParams& p, int64_t m0, int64_t n0) {
+    const int t = threadIdx.x, lane = t & 63;
+    wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t rowbytes = p.K / 2, nblocks = p.K / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 4 * (t >> 6) + i;
+      const int row = 16 * q + (lane >> 2), c = (lane & 3) ^ ((lane >> 4) & 3);
+      a_off[i] = (uint32_t)(min((int64_t)row, p.M - 1 - m0) * rowbytes + 16 * c);
+      w_off[i] = (uint32_t)(min((int64_t)row, p.N - 1 - n0) * rowbytes + 16 * c);
+    }
+    sa_off = (uint32_t)(min((int64_t)t, p.M - 1 - m0) * nblocks);
+    sw_off = (uint32_t)(min((int64_t)t, p.N - 1 - n0) * nblocks);
+    ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_codes + m0 * rowbytes), (short)0, -1, (int)kRsrcWord3);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + n0 * rowbytes), (short)0, -1, (int)kRsrcWord3);
+    rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_scales + m0 * nblocks), (short)0, -1, (int)kRsrcWord3);
+    rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + n0 * nblocks), (short)0, -1, (int)kRsrcWord3);
+  }
+
+  // the kDlLoads loads of the stage at k0 into the stage buffer at `buf`
+  __device__ __forceinline__ void issue(uint8_t* buf, int64_t k0) const {
+    const int kb = (int)(k0 / 2), b0 = (int)(k0 / 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (4 * wv + i) * 1024), 16, a_off[i], kb, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (4 * wv + i) * 1024), 16, w_off[i], kb,
+                                               0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(buf + 2 * kDlCodes + 256 * wv), 4, sa_off, b0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr)(buf + 2 * kDlCodes + BM * 4 + 256 * wv), 4, sw_off, b0,
+                                             0, 0);
+  }
+};
+
+// 8 block-scaled MFMAs of chunk KC, A tiles I0 and I0 + 1 x the 4 W tiles;
+// the lane's scale dwords are pre-shifted, byte 2 KC is the chunk's block
+template <int KC, int I0>
+__device__ __forceinline__ void mx_mfma_half_dl(const uint4 (&ca)[4], const uint4 (&cw)[4], const uint32_t (&sa)[4],
+                                                const uint32_t (&sw)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = I0; i < I0 + 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x8 a = {(int)ca[i].x, (int)ca[i].y, (int)ca[i].z, (int)ca[i].w, 0, 0, 0, 0};
+      const i32x8 b = {(int)cw[j].x, (int)cw[j].y, (int)cw[j].z, (int)cw[j].w, 0, 0, 0, 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, 2 * KC, (int)sa[i], 2 * KC,
+                                                                  (int)sw[j]);
+    }
+}
+
+// LDS addresses of a wave's fragment reads, relative to a stage buffer
+struct DlAddr {
+  uint32_t a[2], w[2];  // code fragment of tile 0, chunk kc
+  uint32_t sa, sw;      // scale dword of tile 0's row
+  int sh;               // 8 kh: the lane's scale byte shift
+};
+
+struct DlRegs {
+  uint4 ca0[4], cw0[4], ca1[4], cw1[4];
+  uint32_t sa[4], sw[4], qa[4], qw[4];
+};
+
+// the stage's scale dwords of the wave's 4 A and 4 W tiles (shifted by the
+// stage that uses them, so that the reads are not waited for here)
+__device__ __forceinline__ void dl_read_scales(const uint8_t* buf, const DlAddr& ad, uint32_t (&ra)[4],
+                                               uint32_t (&rw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = *(const uint32_t*)(buf + ad.sa + i * 128);
+    rw[i] = *(const uint32_t*)(buf + ad.sw + i * 128);
+  }
+}
+
+__device__ __forceinline__ void dl_read_codes(const uint8_t* buf, const DlAddr& ad, int kc, uint4 (&ca)[4],
+                                              uint4 (&cw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ca[i] = *(const uint4*)(buf + ad.a[kc] + i * 2048);
+    cw[i] = *(const uint4*)(buf + ad.w[kc] + i * 2048);
+  }
+}
+
+// One stage.  cur: this stage's buffer; nxt: stage s + 1's; ld: the buffer the
+// loads of stage s + 3 go to (ISSUE).  The three are distinct buffers of the
+// ring, and `__restrict__` tells the compiler so: it then orders the LDS
+// reads only after the loads into the same buffer, which the explicit waits
+// and barrier below already complete.  WAITN: this wave's loads left in
+// flight (those of stages s + 2 and s + 3) when stage s + 1's must have landed.
+//   step 0: issue the loads of stage s + 3, read this stage's chunk-1 codes,
+//           shift this stage's scale dwords, chunk 0 x tiles 0-1;
+//   step 1: chunk 0 x tiles 2-3; wait for stage s + 1's loads; barrier;
+//   step 2: read stage s + 1's scales and chunk-0 codes (NEXT), chunk 1 x
+//           tiles 0-1;
+//   step 3: chunk 1 x tiles 2-3.
+template <bool ISSUE, int WAITN, bool NEXT>
+__device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const uint8_t* __restrict__ nxt,
+                                         uint8_t* __restrict__ ld, const DlLoader& L, int64_t k_ld,
+                                         const DlAddr& ad, DlRegs& r, f32x16 (&acc)[4][4]) {
+  if constexpr (ISSUE) L.issue(ld, k_ld);
+  dl_read_codes(cur, ad, 1, r.ca1, r.cw1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.sa[i] >>= ad.sh;
+    r.sw[i] >>= ad.sh;
+  }
+  mx_mfma_half_dl<0, 0>(r.ca0, r.cw0, r.sa, r.sw, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mx_mfma_half_dl<0, 2>(r.ca0, r.cw0, r.sa, r.sw, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dl_barrier<WAITN>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.qa[i] = r.sa[i];
+    r.qw[i] = r.sw[i];
+  }
+  if constexpr (NEXT) {
+    dl_read_codes(nxt, ad, 0, r.ca0, r.cw0);
+    dl_read_scales(nxt, ad, r.sa, r.sw);
+  }
+  mx_mfma_half_dl<1, 0>(r.ca1, r.cw1, r.qa, r.qw, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mx_mfma_half_dl<1, 2>(r.ca1, r.cw1, r.qa, r.qw, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// the loads of the first min(ns, 3) stages into buffers 0-2, then stage 0's
+// scales and chunk-0 codes once they have landed
+template <int NPRE>
+__device__ __forceinline__ void dl_prologue(uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                            uint8_t* __restrict__ b2, const DlLoader& L, int64_t kb,
+                                            const DlAddr& ad, DlRegs& r) {
+  L.issue(b0, kb);
+  if constexpr (NPRE > 1) L.issue(b1, kb + BK);
+  if constexpr (NPRE > 2) L.issue(b2, kb + 2 * BK);
+  dl_barrier<(NPRE - 1) * kDlLoads>();
+  dl_read_codes(b0, ad, 0, r.ca0, r.cw0);
+  dl_read_scales(b0, ad, r.sa, r.sw);
+}
+
+__device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm,
+                                           int wn, int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
+  DlLoader L;
+  L.init(p, m0, n0);
+  const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
+  DlAddr ad;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int o = (r32 >> 4) * 1024 + 64 * (r32 & 15) + 16 * ((2 * kc + kh) ^ ((r32 >> 2) & 3));
+    ad.a[kc] = (uint32_t)(o + wm * 4 * 2048);
+    ad.w[kc] = (uint32_t)(kDlCodes + o + wn * 4 * 2048);
+  }
+  ad.sa = (uint32_t)(2 * kDlCodes + (wm * 128 + r32) * 4);
+  ad.sw = (uint32_t)(2 * kDlCodes + BM * 4 + (wn * 128 + r32) * 4);
+  ad.sh = 8 * kh;
+  auto buf = [&](int64_t s) { return smem + (int)(s & 3) * kDlBuf; };
+  const int64_t kb = sbeg * BK, ns = send - sbeg;
+  DlRegs r;
+  if (ns >= 3) dl_prologue<3>(buf(0), buf(1), buf(2), L, kb, ad, r);
+  else if (ns == 2) dl_prologue<2>(buf(0), buf(1), buf(2), L, kb, ad, r);
+  else dl_prologue<1>(buf(0), buf(1), buf(2), L, kb, ad, r);
+  int64_t s = 0;
+  for (; s + 3 < ns; ++s) dl_stage<true, 2 * kDlLoads, true>(buf(s), buf(s + 1), buf(s + 3), L, kb + (s + 3) * BK, ad, r, acc);
+  if (s + 2 < ns) {
+    dl_stage<false, kDlLoads, true>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
+    ++s;
+  }
+  if (s + 1 < ns) {
+    dl_stage<false, 0, true>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
+    ++s;
+  }
+  dl_stage<false, 0, false>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
+}
+
 // ---------------------------------------------------------------- kernel
 // FA, FW: operand formats; FA == MXFP4 selects the block-scaled FP4 MFMA path
 template <int FA, int FW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(GemmParams p) {
   constexpr bool MX = (FA == MXFP4);
-  __shared__ __align__(16) uint8_t smem[kNbuf * kBufBytes];
+  static_assert(kNbuf * kBufBytes <= kDlLds, "the register-staged layout fits the LDS-DMA ring");
+  __shared__ __align__(16) uint8_t smem[MX ? kDlLds : kNbuf * kBufBytes];
   // workgroup = (tile, K-split); split s owns stages [s * per, (s + 1) * per)
   const int split = (int)(blockIdx.x % (unsigned)p.splits);
   int tm, tn;
@@ -713,6 +932,9 @@ void gemm_tile_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
   if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+  else if (p.K % BK == 0 && ((((uintptr_t)p.a_codes | (uintptr_t)p.w_codes) & 15) == 0) &&
+           ((((uintptr_t)p.a_scales | (uintptr_t)p.w_scales) & 3) == 0))
+    mx_tile_dl(p, m0, n0, smem, wm, wn, sbeg, send, acc);
   else mx_tile(p, m0, n0, smem, wm, wn, sbeg, send, acc);
 
   const float ga = p.a_global ? *p.a_global : 1.0f;
