@@ -689,12 +689,11 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
 }
 
 // ---------------------------------------------------------------- MXFP4 K loop, LDS-DMA staging
-// For MXFP4 with whole stages (K % 128 == 0), 16-byte aligned code rows and
-// word-aligned scale rows.  Global loads write LDS directly (buffer_load ...
-// lds: lane l of a load lands at 16 l, or 4 l, bytes past the wave's LDS
-// address), so staging needs no registers and no LDS store instructions, and
-// a ring of four stage buffers lets the loads of stage s + 3 start at the top
-// of stage s.
+// For MXFP4 with K % 512 == 0, 16-byte aligned code and scale rows.  Global
+// loads write LDS directly (buffer_load ... lds: lane l of a load lands 16 l
+// bytes past the wave's LDS address), so staging needs no registers and no
+// LDS store instructions, and a ring of four stage buffers lets the loads of
+// stage s + 3 start at the top of stage s.
 //   codes: 1 KiB block q holds rows 16 q .. 16 q + 15 (the stage's 64 bytes
 //     of each), row 16 q + r16's chunk c at slot 64 q + 4 r16 + (c ^ ((r16 >>
 //     2) & 3)).  Load unit q (one wave instruction) fills block q: lane l
@@ -702,14 +701,17 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
 //     lanes read one row's 64 bytes.  A fragment read of tile g, chunk kc
 //     (lane (r32, kh): row 32 g + r32, chunk 2 kc + kh) covers blocks 2 g and
 //     2 g + 1, and any 16 consecutive lanes hit 16 distinct slots mod 16.
-//   scales: the stage's four E8M0 bytes of each row as one dword (row r at
-//     4 r); lane (r32, kh) shifts its row's dword right by 8 kh, so that the
-//     MFMA's byte select 2 kc picks block 2 kc + kh.
-constexpr int kDlCodes = BM * KB;                  // 16 KiB per operand
-constexpr int kDlBuf = 2 * kDlCodes + 2 * BM * 4;  // 34 KiB
+//   scales: loaded per group of four stages, 16 bytes of each row (the four
+//     stages' E8M0 bytes, four per stage) at 16 r, in two group buffers.
+//     Lane (r32, kh) reads its row's dword of the stage and shifts it right
+//     by 8 kh, so that the MFMA's byte select 2 kc picks block 2 kc + kh.
+constexpr int kDlCodes = BM * KB;                          // 16 KiB per operand per stage
+constexpr int kDlBuf = 2 * kDlCodes;                       // 32 KiB
 constexpr int kDlNbuf = 4;
-constexpr int kDlLds = kDlNbuf * kDlBuf;           // 136 KiB
-constexpr int kDlLoads = 10;                       // load instructions per wave per stage
+constexpr int kDlGroup = 4;                                // stages per scale load
+constexpr int kDlScales = 2 * BM * 16;                     // one group's scales, both operands: 8 KiB
+constexpr int kDlLds = kDlNbuf * kDlBuf + 2 * kDlScales;   // 144 KiB
+constexpr int kDlCodeLoads = 8;                            // per wave per stage
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Workgroup barrier of the LDS-DMA ring: this wave's LDS reads complete and
@@ -751,9 +753,9 @@ struct DlLoader {
     rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + n0 * nblocks), (short)0, -1, (int)kRsrcWord3);
   }
 
-  // the kDlLoads loads of the stage at k0 into the stage buffer at `buf`
-  __device__ __forceinline__ void issue(uint8_t* buf, int64_t k0) const {
-    const int kb = (int)(k0 / 2), b0 = (int)(k0 / 32);
+  // the kDlCodeLoads code loads of the stage at k0 into the stage buffer `buf`
+  __device__ __forceinline__ void issue_codes(uint8_t* buf, int64_t k0) const {
+    const int kb = (int)(k0 / 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (4 * wv + i) * 1024), 16, a_off[i], kb, 0, 0);
@@ -761,9 +763,14 @@ struct DlLoader {
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (4 * wv + i) * 1024), 16, w_off[i], kb,
                                                0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(buf + 2 * kDlCodes + 256 * wv), 4, sa_off, b0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr)(buf + 2 * kDlCodes + BM * 4 + 256 * wv), 4, sw_off, b0,
-                                             0, 0);
+  }
+
+  // the two scale loads (A, W) of the group of stages starting at k0 into the
+  // group buffer `sbuf`: rows 64 wv + lane, 16 bytes each
+  __device__ __forceinline__ void issue_scales(uint8_t* sbuf, int64_t k0) const {
+    const int b0 = (int)(k0 / 32);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(sbuf + 1024 * wv), 16, sa_off, b0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr)(sbuf + BM * 16 + 1024 * wv), 16, sw_off, b0, 0, 0);
   }
 };
 
@@ -783,10 +790,11 @@ __device__ __forceinline__ void mx_mfma_half_dl(const uint4 (&ca)[4], const uint
     }
 }
 
-// LDS addresses of a wave's fragment reads, relative to a stage buffer
+// LDS addresses of a wave's fragment and scale reads, relative to a stage
+// buffer (codes) or a group buffer (scales)
 struct DlAddr {
   uint32_t a[2], w[2];  // code fragment of tile 0, chunk kc
-  uint32_t sa, sw;      // scale dword of tile 0's row
+  uint32_t sa, sw;      // 16-byte scale row of tile 0's row
   int sh;               // 8 kh: the lane's scale byte shift
 };
 
@@ -795,14 +803,16 @@ struct DlRegs {
   uint32_t sa[4], sw[4], qa[4], qw[4];
 };
 
-// the stage's scale dwords of the wave's 4 A and 4 W tiles (shifted by the
-// stage that uses them, so that the reads are not waited for here)
-__device__ __forceinline__ void dl_read_scales(const uint8_t* buf, const DlAddr& ad, uint32_t (&ra)[4],
+// the scale dwords of stage PH of a group for the wave's 4 A and 4 W tiles
+// (shifted by the stage that uses them, so that the reads are not waited for
+// here)
+template <int PH>
+__device__ __forceinline__ void dl_read_scales(const uint8_t* sbuf, const DlAddr& ad, uint32_t (&ra)[4],
                                                uint32_t (&rw)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ra[i] = *(const uint32_t*)(buf + ad.sa + i * 128);
-    rw[i] = *(const uint32_t*)(buf + ad.sw + i * 128);
+    ra[i] = *(const uint32_t*)(sbuf + ad.sa + i * 512 + 4 * PH);
+    rw[i] = *(const uint32_t*)(sbuf + ad.sw + i * 512 + 4 * PH);
   }
 }
 
@@ -815,23 +825,28 @@ __device__ __forceinline__ void dl_read_codes(const uint8_t* buf, const DlAddr& 
   }
 }
 
-// One stage.  cur: this stage's buffer; nxt: stage s + 1's; ld: the buffer the
-// loads of stage s + 3 go to (ISSUE).  The three are distinct buffers of the
-// ring, and `__restrict__` tells the compiler so: it then orders the LDS
-// reads only after the loads into the same buffer, which the explicit waits
-// and barrier below already complete.  WAITN: this wave's loads left in
-// flight (those of stages s + 2 and s + 3) when stage s + 1's must have landed.
-//   step 0: issue the loads of stage s + 3, read this stage's chunk-1 codes,
-//           shift this stage's scale dwords, chunk 0 x tiles 0-1;
-//   step 1: chunk 0 x tiles 2-3; wait for stage s + 1's loads; barrier;
-//   step 2: read stage s + 1's scales and chunk-0 codes (NEXT), chunk 1 x
+// One stage s.  cur: stage s's buffer; nxt: stage s + 1's; ld: where the code
+// loads of stage s + 3 go (ISSUE); srd: the scale group buffer of stage s + 1,
+// whose dwords sit at phase PHN; sld: where the next group's scales go
+// (SCALES).  These are distinct buffers, and `__restrict__` tells the
+// compiler so: it then orders the LDS reads only after the loads into the
+// same buffer, which the explicit waits and barrier below already complete.
+// WAITN: this wave's loads left in flight when stage s + 1's codes and scales
+// must have landed.
+//   step 0: issue the code loads of stage s + 3 (and the next group's scale
+//           loads), read stage s's chunk-1 codes, shift stage s's scale
+//           dwords, chunk 0 x tiles 0-1;
+//   step 1: chunk 0 x tiles 2-3; wait; barrier;
+//   step 2: read stage s + 1's chunk-0 codes and scales (NEXT), chunk 1 x
 //           tiles 0-1;
 //   step 3: chunk 1 x tiles 2-3.
-template <bool ISSUE, int WAITN, bool NEXT>
+template <bool ISSUE, bool SCALES, int WAITN, bool NEXT, int PHN>
 __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const uint8_t* __restrict__ nxt,
-                                         uint8_t* __restrict__ ld, const DlLoader& L, int64_t k_ld,
+                                         uint8_t* __restrict__ ld, const uint8_t* __restrict__ srd,
+                                         uint8_t* __restrict__ sld, const DlLoader& L, int64_t k_ld, int64_t k_sc,
                                          const DlAddr& ad, DlRegs& r, f32x16 (&acc)[4][4]) {
-  if constexpr (ISSUE) L.issue(ld, k_ld);
+  if constexpr (ISSUE) L.issue_codes(ld, k_ld);
+  if constexpr (SCALES) L.issue_scales(sld, k_sc);
   dl_read_codes(cur, ad, 1, r.ca1, r.cw1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -850,7 +865,7 @@ __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const 
   }
   if constexpr (NEXT) {
     dl_read_codes(nxt, ad, 0, r.ca0, r.cw0);
-    dl_read_scales(nxt, ad, r.sa, r.sw);
+    dl_read_scales<PHN>(srd, ad, r.sa, r.sw);
   }
   mx_mfma_half_dl<1, 0>(r.ca1, r.cw1, r.qa, r.qw, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -858,20 +873,29 @@ __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// the loads of the first min(ns, 3) stages into buffers 0-2, then stage 0's
-// scales and chunk-0 codes once they have landed
-template <int NPRE>
+// group 0's scales and the codes of stages 0-2, then stage 0's scales and
+// chunk-0 codes once they have landed (the codes of stages 1 and 2 may stay in
+// flight)
 __device__ __forceinline__ void dl_prologue(uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
-                                            uint8_t* __restrict__ b2, const DlLoader& L, int64_t kb,
-                                            const DlAddr& ad, DlRegs& r) {
-  L.issue(b0, kb);
-  if constexpr (NPRE > 1) L.issue(b1, kb + BK);
-  if constexpr (NPRE > 2) L.issue(b2, kb + 2 * BK);
-  dl_barrier<(NPRE - 1) * kDlLoads>();
+                                            uint8_t* __restrict__ b2, uint8_t* __restrict__ sb0, const DlLoader& L,
+                                            int64_t kb, const DlAddr& ad, DlRegs& r) {
+  L.issue_scales(sb0, kb);
+  L.issue_codes(b0, kb);
+  L.issue_codes(b1, kb + BK);
+  L.issue_codes(b2, kb + 2 * BK);
+  dl_barrier<2 * kDlCodeLoads>();
   dl_read_codes(b0, ad, 0, r.ca0, r.cw0);
-  dl_read_scales(b0, ad, r.sa, r.sw);
+  dl_read_scales<0>(sb0, ad, r.sa, r.sw);
 }
 
+// ns = send - sbeg is a positive multiple of kDlGroup (whole scale groups).
+// Loads in flight per wave, in issue order: stage s issues the codes of s + 3
+// (8 loads) and, at phase 1 of group g, group g + 1's scales (2 loads) right
+// after them.  When stage s + 1 must have landed, the loads allowed in flight
+// are the codes of s + 2 and s + 3 plus any scale loads issued after the
+// codes of s + 1 for a group s + 1 does not belong to: 16 at phases 0 and 3,
+// 18 at phases 1 and 2.  The last group issues no scales, and only its first
+// stage issues codes.
 __device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm,
                                            int wn, int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
   DlLoader L;
@@ -884,26 +908,35 @@ __device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int6
     ad.a[kc] = (uint32_t)(o + wm * 4 * 2048);
     ad.w[kc] = (uint32_t)(kDlCodes + o + wn * 4 * 2048);
   }
-  ad.sa = (uint32_t)(2 * kDlCodes + (wm * 128 + r32) * 4);
-  ad.sw = (uint32_t)(2 * kDlCodes + BM * 4 + (wn * 128 + r32) * 4);
+  ad.sa = (uint32_t)((wm * 128 + r32) * 16);
+  ad.sw = (uint32_t)(BM * 16 + (wn * 128 + r32) * 16);
   ad.sh = 8 * kh;
   auto buf = [&](int64_t s) { return smem + (int)(s & 3) * kDlBuf; };
-  const int64_t kb = sbeg * BK, ns = send - sbeg;
+  auto sbuf = [&](int64_t g) { return smem + kDlNbuf * kDlBuf + (int)(g & 1) * kDlScales; };
+  const int64_t kb = sbeg * BK, ns = send - sbeg, ng = ns / kDlGroup;
   DlRegs r;
-  if (ns >= 3) dl_prologue<3>(buf(0), buf(1), buf(2), L, kb, ad, r);
-  else if (ns == 2) dl_prologue<2>(buf(0), buf(1), buf(2), L, kb, ad, r);
-  else dl_prologue<1>(buf(0), buf(1), buf(2), L, kb, ad, r);
-  int64_t s = 0;
-  for (; s + 3 < ns; ++s) dl_stage<true, 2 * kDlLoads, true>(buf(s), buf(s + 1), buf(s + 3), L, kb + (s + 3) * BK, ad, r, acc);
-  if (s + 2 < ns) {
-    dl_stage<false, kDlLoads, true>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
-    ++s;
+  dl_prologue(buf(0), buf(1), buf(2), sbuf(0), L, kb, ad, r);
+  constexpr int C2 = 2 * kDlCodeLoads;
+  int64_t g = 0;
+  for (; g + 1 < ng; ++g) {
+    const int64_t s = kDlGroup * g;
+    const int64_t kn = kb + (s + kDlGroup) * BK;  // the next group's first stage
+    dl_stage<true, false, C2, true, 1>(buf(s), buf(s + 1), buf(s + 3), sbuf(g), sbuf(g + 1), L,
+                                       kb + (s + 3) * BK, kn, ad, r, acc);
+    dl_stage<true, true, C2 + 2, true, 2>(buf(s + 1), buf(s + 2), buf(s + 4), sbuf(g), sbuf(g + 1), L,
+                                          kb + (s + 4) * BK, kn, ad, r, acc);
+    dl_stage<true, false, C2 + 2, true, 3>(buf(s + 2), buf(s + 3), buf(s + 5), sbuf(g), sbuf(g + 1), L,
+                                           kb + (s + 5) * BK, kn, ad, r, acc);
+    dl_stage<true, false, C2, true, 0>(buf(s + 3), buf(s + 4), buf(s + 6), sbuf(g + 1), sbuf(g), L,
+                                       kb + (s + 6) * BK, kn, ad, r, acc);
   }
-  if (s + 1 < ns) {
-    dl_stage<false, 0, true>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
-    ++s;
-  }
-  dl_stage<false, 0, false>(buf(s), buf(s + 1), buf(s + 3), L, 0, ad, r, acc);
+  const int64_t s = kDlGroup * g;  // the last group
+  dl_stage<true, false, C2, true, 1>(buf(s), buf(s + 1), buf(s + 3), sbuf(g), sbuf(g + 1), L, kb + (s + 3) * BK, 0,
+                                     ad, r, acc);
+  dl_stage<false, false, kDlCodeLoads, true, 2>(buf(s + 1), buf(s + 2), buf(s + 4), sbuf(g), sbuf(g + 1), L, 0, 0,
+                                                ad, r, acc);
+  dl_stage<false, false, 0, true, 3>(buf(s + 2), buf(s + 3), buf(s + 5), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r, acc);
+  dl_stage<false, false, 0, false, 0>(buf(s + 3), buf(s + 4), buf(s + 6), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r, acc);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -918,7 +951,13 @@ void gemm_tile_kernel(GemmParams p) {
   const int split = (int)(blockIdx.x % (unsigned)p.splits);
   int tm, tn;
   tile_coords(p.M, p.N, (int)(blockIdx.x / (unsigned)p.splits), tm, tn);
-  const int64_t nst = (p.K + BK - 1) / BK, per = (nst + p.splits - 1) / p.splits;
+  // the MXFP4 LDS-DMA path takes whole groups of kDlGroup stages per split
+  const bool dl = MX && p.K % (kDlGroup * BK) == 0 &&
+                  ((((uintptr_t)p.a_codes | (uintptr_t)p.w_codes | (uintptr_t)p.a_scales | (uintptr_t)p.w_scales) &
+                    15) == 0);
+  const int64_t nst = (p.K + BK - 1) / BK;
+  int64_t per = (nst + p.splits - 1) / p.splits;
+  if (dl) per = (per + kDlGroup - 1) / kDlGroup * kDlGroup;
   const int64_t sbeg = min(nst, split * per), send = min(nst, sbeg + per);
   if (sbeg >= send) return;  // no stages left for this split (uniform across the workgroup)
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -932,9 +971,7 @@ void gemm_tile_kernel(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
   if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
-  else if (p.K % BK == 0 && ((((uintptr_t)p.a_codes | (uintptr_t)p.w_codes) & 15) == 0) &&
-           ((((uintptr_t)p.a_scales | (uintptr_t)p.w_scales) & 3) == 0))
-    mx_tile_dl(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+  else if (dl) mx_tile_dl(p, m0, n0, smem, wm, wn, sbeg, send, acc);
   else mx_tile(p, m0, n0, smem, wm, wn, sbeg, send, acc);
 
   const float ga = p.a_global ? *p.a_global : 1.0f;

@@ -92,6 +92,24 @@ def test_gemm_decode_shapes(B, fa, fw, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
+# MXFP4 shapes with K % 512 == 0 (the LDS-DMA staging path, scales loaded per
+# group of four 128-element stages): ragged M and N, one group (K = 512),
+# FP32 output with few tiles (K splits rounded to whole groups, some splits
+# left empty) and bf16 output
+@pytest.mark.parametrize("M,N,K", [(300, 260, 1024), (64, 96, 2048), (257, 129, 512), (33, 300, 1536)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_mxfp4_group_staging(B, M, N, K, out_dtype):
+    a = datagen.student_t((M, K), 920 + M, 4.0)
+    w = datagen.normal((N, K), 921 + N, 0.02)
+    ca, sa, ga = oquant(a, "mxfp4")
+    cw, sw, gw = oquant(w, "mxfp4")
+    ref = O.gemm_rows("mxfp4", ca, sa, ga, "mxfp4", cw, sw, gw, None, M, N, K)
+    case(f"gemm mxfp4 group staging {M}x{N}x{K} {out_dtype}")
+    got = gpu_gemm(B, "mxfp4", ca, sa, ga, "mxfp4", cw, sw, gw, None, out_dtype)
+    tol = TOL if out_dtype == "f32" else 8e-3
+    assert rel_fro(got, ref) <= tol
+
+
 def _high_low_word_offset(lo, nbytes):
     """Byte offset (a multiple of 256) from an address whose low 32 bits are
     `lo` to the first one whose low 32 bits lie in [2^31, 2^32 - nbytes]."""
