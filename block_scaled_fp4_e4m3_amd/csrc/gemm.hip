@@ -692,26 +692,28 @@ __device__ __forceinline__ void mx_tile(const GemmParams& p, int64_t m0, int64_t
 // For MXFP4 with K % 512 == 0, 16-byte aligned code and scale rows.  Global
 // loads write LDS directly (buffer_load ... lds: lane l of a load lands 16 l
 // bytes past the wave's LDS address), so staging needs no registers and no
-// LDS store instructions, and a ring of four stage buffers lets the loads of
-// stage s + 3 start at the top of stage s.
-//   codes: 1 KiB block q holds rows 16 q .. 16 q + 15 (the stage's 64 bytes
-//     of each), row 16 q + r16's chunk c at slot 64 q + 4 r16 + (c ^ ((r16 >>
-//     2) & 3)).  Load unit q (one wave instruction) fills block q: lane l
-//     fetches row 16 q + l / 4, chunk (l % 4) ^ ((l / 16) % 4), so each four
-//     lanes read one row's 64 bytes.  A fragment read of tile g, chunk kc
-//     (lane (r32, kh): row 32 g + r32, chunk 2 kc + kh) covers blocks 2 g and
-//     2 g + 1, and any 16 consecutive lanes hit 16 distinct slots mod 16.
+// LDS store instructions.  Codes are loaded per pair of stages (128 bytes,
+// one cache line, of each row) into two pair buffers; the loads of pair
+// (s + 3) / 2 start right after the barrier of odd stage s.
+//   codes: 1 KiB block B holds rows 8 B .. 8 B + 7, 16-byte chunk ch (0-3:
+//     the pair's first stage, 4-7: its second) of row 8 B + r7 at slot
+//     64 B + 8 r7 + (ch ^ x), x = (r7 / 2) | (B % 2) * 4.  Load unit B (one
+//     wave instruction) fills block B: lane l fetches row 8 B + l / 8, chunk
+//     (l % 8) ^ x, so each eight lanes read one row's line.  A fragment read
+//     of tile g, chunk kc of half h (lane (r32, kh): row 32 g + r32, chunk
+//     4 h + 2 kc + kh) covers blocks 4 g .. 4 g + 3, and any 16 consecutive
+//     lanes hit 16 distinct slots mod 16.
 //   scales: loaded per group of four stages, 16 bytes of each row (the four
 //     stages' E8M0 bytes, four per stage) at 16 r, in two group buffers.
 //     Lane (r32, kh) reads its row's dword of the stage and shifts it right
 //     by 8 kh, so that the MFMA's byte select 2 kc picks block 2 kc + kh.
-constexpr int kDlCodes = BM * KB;                          // 16 KiB per operand per stage
-constexpr int kDlBuf = 2 * kDlCodes;                       // 32 KiB
-constexpr int kDlNbuf = 4;
+constexpr int kDlCodes = BM * 2 * KB;                      // 32 KiB per operand per pair of stages
+constexpr int kDlBuf = 2 * kDlCodes;                       // 64 KiB
+constexpr int kDlNbuf = 2;
 constexpr int kDlGroup = 4;                                // stages per scale load
 constexpr int kDlScales = 2 * BM * 16;                     // one group's scales, both operands: 8 KiB
 constexpr int kDlLds = kDlNbuf * kDlBuf + 2 * kDlScales;   // 144 KiB
-constexpr int kDlCodeLoads = 8;                            // per wave per stage
+constexpr int kDlPairLoads = 16;                           // code loads per wave per pair
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Workgroup barrier of the LDS-DMA ring: this wave's LDS reads complete and
@@ -730,7 +732,7 @@ __device__ __forceinline__ void dl_barrier() {
 
 struct DlLoader {
   __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
-  uint32_t a_off[4], w_off[4];  // this lane's row and chunk offsets in its 4 A and 4 W units
+  uint32_t a_off[8], w_off[8];  // this lane's row and chunk offsets in its 8 A and 8 W units
   uint32_t sa_off, sw_off;      // this thread's scale row
   int wv;                       // wave index (uniform)
 
@@ -739,11 +741,11 @@ struct DlLoader {
     wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t rowbytes = p.K / 2, nblocks = p.K / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = 4 * (t >> 6) + i;
-      const int row = 16 * q + (lane >> 2), c = (lane & 3) ^ ((lane >> 4) & 3);
-      a_off[i] = (uint32_t)(min((int64_t)row, p.M - 1 - m0) * rowbytes + 16 * c);
-      w_off[i] = (uint32_t)(min((int64_t)row, p.N - 1 - n0) * rowbytes + 16 * c);
+    for (int j = 0; j < 8; ++j) {
+      const int blk = 8 * (t >> 6) + j, r7 = lane >> 3;
+      const int row = 8 * blk + r7, ch = (lane & 7) ^ ((r7 >> 1) | ((blk & 1) << 2));
+      a_off[j] = (uint32_t)(min((int64_t)row, p.M - 1 - m0) * rowbytes + 16 * ch);
+      w_off[j] = (uint32_t)(min((int64_t)row, p.N - 1 - n0) * rowbytes + 16 * ch);
     }
     sa_off = (uint32_t)(min((int64_t)t, p.M - 1 - m0) * nblocks);
     sw_off = (uint32_t)(min((int64_t)t, p.N - 1 - n0) * nblocks);
@@ -753,15 +755,16 @@ struct DlLoader {
     rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + n0 * nblocks), (short)0, -1, (int)kRsrcWord3);
   }
 
-  // the kDlCodeLoads code loads of the stage at k0 into the stage buffer `buf`
-  __device__ __forceinline__ void issue_codes(uint8_t* buf, int64_t k0) const {
+  // the kDlPairLoads code loads of the pair of stages at k0 into the pair
+  // buffer `buf`: blocks 8 wv .. 8 wv + 7 of each operand
+  __device__ __forceinline__ void issue_pair(uint8_t* buf, int64_t k0) const {
     const int kb = (int)(k0 / 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (4 * wv + i) * 1024), 16, a_off[i], kb, 0, 0);
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (8 * wv + j) * 1024), 16, a_off[j], kb, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (4 * wv + i) * 1024), 16, w_off[i], kb,
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (8 * wv + j) * 1024), 16, w_off[j], kb,
                                                0, 0);
   }
 
@@ -790,10 +793,10 @@ __device__ __forceinline__ void mx_mfma_half_dl(const uint4 (&ca)[4], const uint
     }
 }
 
-// LDS addresses of a wave's fragment and scale reads, relative to a stage
+// LDS addresses of a wave's fragment and scale reads, relative to a pair
 // buffer (codes) or a group buffer (scales)
 struct DlAddr {
-  uint32_t a[2], w[2];  // code fragment of tile 0, chunk kc
+  uint32_t a[2][2], w[2][2];  // code fragment of tile 0, half h, chunk kc
   uint32_t sa, sw;      // 16-byte scale row of tile 0's row
   int sh;               // 8 kh: the lane's scale byte shift
 };
@@ -816,38 +819,38 @@ __device__ __forceinline__ void dl_read_scales(const uint8_t* sbuf, const DlAddr
   }
 }
 
-__device__ __forceinline__ void dl_read_codes(const uint8_t* buf, const DlAddr& ad, int kc, uint4 (&ca)[4],
-                                              uint4 (&cw)[4]) {
+template <int H, int KC>
+__device__ __forceinline__ void dl_read_codes(const uint8_t* buf, const DlAddr& ad, uint4 (&ca)[4], uint4 (&cw)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ca[i] = *(const uint4*)(buf + ad.a[kc] + i * 2048);
-    cw[i] = *(const uint4*)(buf + ad.w[kc] + i * 2048);
+    ca[i] = *(const uint4*)(buf + ad.a[H][KC] + i * 4096);
+    cw[i] = *(const uint4*)(buf + ad.w[H][KC] + i * 4096);
   }
 }
 
-// One stage s.  cur: stage s's buffer; nxt: stage s + 1's; ld: where the code
-// loads of stage s + 3 go (ISSUE); srd: the scale group buffer of stage s + 1,
-// whose dwords sit at phase PHN; sld: where the next group's scales go
-// (SCALES).  These are distinct buffers, and `__restrict__` tells the
-// compiler so: it then orders the LDS reads only after the loads into the
-// same buffer, which the explicit waits and barrier below already complete.
-// WAITN: this wave's loads left in flight when stage s + 1's codes and scales
-// must have landed.
-//   step 0: issue the code loads of stage s + 3 (and the next group's scale
-//           loads), read stage s's chunk-1 codes, shift stage s's scale
-//           dwords, chunk 0 x tiles 0-1;
+// One stage s, half H of its pair.  cur: the pair buffer of stage s; nxt:
+// that of stage s + 1 (half HN); ld: where the code loads of pair (s + 3) / 2
+// go (ISSUE, odd s: the buffer of stage s's pair, whose last read is this
+// stage's step 0); srd: the scale group buffer of stage s + 1, whose dwords
+// sit at phase PHN; sld: where the next group's scales go (SCALES).  The
+// accesses through these pointers that `__restrict__` declares disjoint are:
+// the code loads into ld and the reads of nxt, srd; the scale loads into sld
+// and the reads of srd, nxt.  The reads of cur come before the barrier, the
+// loads after it.  WAITN: this wave's loads left in flight when stage s + 1's
+// codes and scales must have landed.
+//   step 0: read stage s's chunk-1 codes, shift stage s's scale dwords, chunk
+//           0 x tiles 0-1;
 //   step 1: chunk 0 x tiles 2-3; wait; barrier;
-//   step 2: read stage s + 1's chunk-0 codes and scales (NEXT), chunk 1 x
-//           tiles 0-1;
+//   step 2: issue the code loads of pair (s + 3) / 2 and the next group's
+//           scale loads, read stage s + 1's chunk-0 codes and scales (NEXT),
+//           chunk 1 x tiles 0-1;
 //   step 3: chunk 1 x tiles 2-3.
-template <bool ISSUE, bool SCALES, int WAITN, bool NEXT, int PHN>
+template <bool ISSUE, bool SCALES, int WAITN, bool NEXT, int H, int HN, int PHN>
 __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const uint8_t* __restrict__ nxt,
                                          uint8_t* __restrict__ ld, const uint8_t* __restrict__ srd,
                                          uint8_t* __restrict__ sld, const DlLoader& L, int64_t k_ld, int64_t k_sc,
                                          const DlAddr& ad, DlRegs& r, f32x16 (&acc)[4][4]) {
-  if constexpr (ISSUE) L.issue_codes(ld, k_ld);
-  if constexpr (SCALES) L.issue_scales(sld, k_sc);
-  dl_read_codes(cur, ad, 1, r.ca1, r.cw1);
+  dl_read_codes<H, 1>(cur, ad, r.ca1, r.cw1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     r.sa[i] >>= ad.sh;
@@ -863,8 +866,10 @@ __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const 
     r.qa[i] = r.sa[i];
     r.qw[i] = r.sw[i];
   }
+  if constexpr (ISSUE) L.issue_pair(ld, k_ld);
+  if constexpr (SCALES) L.issue_scales(sld, k_sc);
   if constexpr (NEXT) {
-    dl_read_codes(nxt, ad, 0, r.ca0, r.cw0);
+    dl_read_codes<HN, 0>(nxt, ad, r.ca0, r.cw0);
     dl_read_scales<PHN>(srd, ad, r.sa, r.sw);
   }
   mx_mfma_half_dl<1, 0>(r.ca1, r.cw1, r.qa, r.qw, acc);
@@ -873,70 +878,71 @@ __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// group 0's scales and the codes of stages 0-2, then stage 0's scales and
-// chunk-0 codes once they have landed (the codes of stages 1 and 2 may stay in
-// flight)
+// group 0's scales and the codes of pairs 0 and 1, then stage 0's scales and
+// chunk-0 codes once they have landed (pair 1 may stay in flight)
 __device__ __forceinline__ void dl_prologue(uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
-                                            uint8_t* __restrict__ b2, uint8_t* __restrict__ sb0, const DlLoader& L,
-                                            int64_t kb, const DlAddr& ad, DlRegs& r) {
+                                            uint8_t* __restrict__ sb0, const DlLoader& L, int64_t kb,
+                                            const DlAddr& ad, DlRegs& r) {
   L.issue_scales(sb0, kb);
-  L.issue_codes(b0, kb);
-  L.issue_codes(b1, kb + BK);
-  L.issue_codes(b2, kb + 2 * BK);
-  dl_barrier<2 * kDlCodeLoads>();
-  dl_read_codes(b0, ad, 0, r.ca0, r.cw0);
+  L.issue_pair(b0, kb);
+  L.issue_pair(b1, kb + 2 * BK);
+  dl_barrier<kDlPairLoads>();
+  dl_read_codes<0, 0>(b0, ad, r.ca0, r.cw0);
   dl_read_scales<0>(sb0, ad, r.sa, r.sw);
 }
 
 // ns = send - sbeg is a positive multiple of kDlGroup (whole scale groups).
-// Loads in flight per wave, in issue order: stage s issues the codes of s + 3
-// (8 loads) and, at phase 1 of group g, group g + 1's scales (2 loads) right
-// after them.  When stage s + 1 must have landed, the loads allowed in flight
-// are the codes of s + 2 and s + 3 plus any scale loads issued after the
-// codes of s + 1 for a group s + 1 does not belong to: 16 at phases 0 and 3,
-// 18 at phases 1 and 2.  The last group issues no scales, and only its first
-// stage issues codes.
+// Loads in flight per wave, in issue order: odd stage s issues, after its
+// barrier, the codes of pair (s + 3) / 2 (16 loads) and, at phase 1 of group
+// g, group g + 1's scales (2 loads).  When stage s + 1 must have landed, the
+// loads allowed in flight are those issued after the ones it needs: 16 at
+// phase 0 (the next pair), none at phase 1, 18 at phase 2 (the next pair and
+// group), none at phase 3.  The last group issues nothing.
 __device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm,
                                            int wn, int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
   DlLoader L;
   L.init(p, m0, n0);
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
   DlAddr ad;
+  const int r7 = r32 & 7, x = (r7 >> 1) | (((r32 >> 3) & 1) << 2);
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-    const int o = (r32 >> 4) * 1024 + 64 * (r32 & 15) + 16 * ((2 * kc + kh) ^ ((r32 >> 2) & 3));
-    ad.a[kc] = (uint32_t)(o + wm * 4 * 2048);
-    ad.w[kc] = (uint32_t)(kDlCodes + o + wn * 4 * 2048);
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int o = (r32 >> 3) * 1024 + 128 * r7 + 16 * ((4 * h + 2 * kc + kh) ^ x);
+      ad.a[h][kc] = (uint32_t)(o + wm * 16 * 1024);
+      ad.w[h][kc] = (uint32_t)(kDlCodes + o + wn * 16 * 1024);
+    }
   ad.sa = (uint32_t)((wm * 128 + r32) * 16);
   ad.sw = (uint32_t)(BM * 16 + (wn * 128 + r32) * 16);
   ad.sh = 8 * kh;
-  auto buf = [&](int64_t s) { return smem + (int)(s & 3) * kDlBuf; };
+  auto pbuf = [&](int64_t pr) { return smem + (int)(pr & 1) * kDlBuf; };
   auto sbuf = [&](int64_t g) { return smem + kDlNbuf * kDlBuf + (int)(g & 1) * kDlScales; };
   const int64_t kb = sbeg * BK, ns = send - sbeg, ng = ns / kDlGroup;
   DlRegs r;
-  dl_prologue(buf(0), buf(1), buf(2), sbuf(0), L, kb, ad, r);
-  constexpr int C2 = 2 * kDlCodeLoads;
+  dl_prologue(pbuf(0), pbuf(1), sbuf(0), L, kb, ad, r);
+  constexpr int P = kDlPairLoads;
   int64_t g = 0;
   for (; g + 1 < ng; ++g) {
-    const int64_t s = kDlGroup * g;
-    const int64_t kn = kb + (s + kDlGroup) * BK;  // the next group's first stage
-    dl_stage<true, false, C2, true, 1>(buf(s), buf(s + 1), buf(s + 3), sbuf(g), sbuf(g + 1), L,
-                                       kb + (s + 3) * BK, kn, ad, r, acc);
-    dl_stage<true, true, C2 + 2, true, 2>(buf(s + 1), buf(s + 2), buf(s + 4), sbuf(g), sbuf(g + 1), L,
-                                          kb + (s + 4) * BK, kn, ad, r, acc);
-    dl_stage<true, false, C2 + 2, true, 3>(buf(s + 2), buf(s + 3), buf(s + 5), sbuf(g), sbuf(g + 1), L,
-                                           kb + (s + 5) * BK, kn, ad, r, acc);
-    dl_stage<true, false, C2, true, 0>(buf(s + 3), buf(s + 4), buf(s + 6), sbuf(g + 1), sbuf(g), L,
-                                       kb + (s + 6) * BK, kn, ad, r, acc);
+    const int64_t pr = 2 * g, s = kDlGroup * g;
+    dl_stage<false, false, P, true, 0, 1, 1>(pbuf(pr), pbuf(pr), pbuf(pr + 1), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r,
+                                            acc);
+    dl_stage<true, true, 0, true, 1, 0, 2>(pbuf(pr), pbuf(pr + 1), pbuf(pr + 2), sbuf(g), sbuf(g + 1), L,
+                                           kb + (s + 4) * BK, kb + (s + 4) * BK, ad, r, acc);
+    dl_stage<false, false, P + 2, true, 0, 1, 3>(pbuf(pr + 1), pbuf(pr + 1), pbuf(pr + 2), sbuf(g), sbuf(g + 1), L,
+                                                0, 0, ad, r, acc);
+    dl_stage<true, false, 0, true, 1, 0, 0>(pbuf(pr + 1), pbuf(pr + 2), pbuf(pr + 3), sbuf(g + 1), sbuf(g), L,
+                                            kb + (s + 6) * BK, 0, ad, r, acc);
   }
-  const int64_t s = kDlGroup * g;  // the last group
-  dl_stage<true, false, C2, true, 1>(buf(s), buf(s + 1), buf(s + 3), sbuf(g), sbuf(g + 1), L, kb + (s + 3) * BK, 0,
-                                     ad, r, acc);
-  dl_stage<false, false, kDlCodeLoads, true, 2>(buf(s + 1), buf(s + 2), buf(s + 4), sbuf(g), sbuf(g + 1), L, 0, 0,
-                                                ad, r, acc);
-  dl_stage<false, false, 0, true, 3>(buf(s + 2), buf(s + 3), buf(s + 5), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r, acc);
-  dl_stage<false, false, 0, false, 0>(buf(s + 3), buf(s + 4), buf(s + 6), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r, acc);
+  const int64_t pr = 2 * g;  // the last group
+  dl_stage<false, false, P, true, 0, 1, 1>(pbuf(pr), pbuf(pr), pbuf(pr + 1), sbuf(g), sbuf(g + 1), L, 0, 0, ad, r,
+                                          acc);
+  dl_stage<false, false, 0, true, 1, 0, 2>(pbuf(pr), pbuf(pr + 1), pbuf(pr + 2), sbuf(g), sbuf(g + 1), L, 0, 0, ad,
+                                           r, acc);
+  dl_stage<false, false, 0, true, 0, 1, 3>(pbuf(pr + 1), pbuf(pr + 1), pbuf(pr + 2), sbuf(g), sbuf(g + 1), L, 0, 0,
+                                           ad, r, acc);
+  dl_stage<false, false, 0, false, 1, 0, 0>(pbuf(pr + 1), pbuf(pr + 2), pbuf(pr + 3), sbuf(g), sbuf(g + 1), L, 0, 0,
+                                            ad, r, acc);
 }
 
 // ---------------------------------------------------------------- kernel
