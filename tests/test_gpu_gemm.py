@@ -110,6 +110,35 @@ def test_gemm_mxfp4_group_staging(B, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
+# scale rows at any byte alignment (only codes and C must be 16-byte aligned):
+# 16-byte aligned scales take the MXFP4 LDS-DMA path when K % 512 == 0, word
+# aligned ones the register path with word loads, others byte loads
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("off", [0, 1, 4, 8])
+def test_gemm_scale_alignment(B, fmt, off):
+    import torch
+    M, N, K = 200, 300, 1024
+    a = datagen.student_t((M, K), 930 + off, 4.0)
+    w = datagen.normal((N, K), 931 + off, 0.02)
+    ca, sa, ga = oquant(a, fmt)
+    cw, sw, gw = oquant(w, fmt)
+    ref = O.gemm_rows(fmt, ca, sa, ga, fmt, cw, sw, gw, None, M, N, K)
+
+    def shifted(arr):
+        buf = torch.zeros(arr.size + 32, dtype=torch.uint8, device="cuda")
+        v = buf[off:off + arr.size].view(arr.shape)
+        v.copy_(dev(arr))
+        return buf, v
+    bufa, sa_d = shifted(sa)
+    bufw, sw_d = shifted(sw)
+    assert sa_d.data_ptr() % 16 == off and sw_d.data_ptr() % 16 == off
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    case(f"gemm {fmt} {M}x{N}x{K} scales at byte offset {off}")
+    B.gemm(fmt, dev(ca), sa_d, scalar_dev(ga), fmt, dev(cw), sw_d, scalar_dev(gw), None, out=out)
+    torch.cuda.synchronize()
+    assert rel_fro(host(out), ref) <= TOL
+
+
 def _high_low_word_offset(lo, nbytes):
     """Byte offset (a multiple of 256) from an address whose low 32 bits are
     `lo` to the first one whose low 32 bits lie in [2^31, 2^32 - nbytes]."""
