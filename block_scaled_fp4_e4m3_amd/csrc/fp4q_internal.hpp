@@ -23,6 +23,7 @@ struct QuantParams {
   int hadamard;           // 0 or 32
   int prevent_zero;
   float special[4];       // RAZER_W table
+  float fused_denom;      // > 0: one workgroup that first sets *global = amax / fused_denom (automatic g)
 };
 
 struct DequantParams {

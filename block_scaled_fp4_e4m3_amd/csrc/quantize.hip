@@ -595,6 +595,59 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
+// Automatic global scale inside a single-workgroup launch (small tensors,
+// where the separate abs-max, finalize and zeroing launches would dominate):
+// the abs-max of the transformed tensor as an integer maximum of magnitude
+// bits (order-free, so equal to the grid-wide reduction), then amax /
+// fused_denom, or 1 for an all-zero tensor, written to *global.  Every thread
+// returns g.  The chunk width and the Hadamard stage order do not change the
+// transformed values, so the maximum is that of the separate abs-max pass.
+template <int L, bool BF16>
+__device__ float fused_auto_global(const QuantParams& p) {
+  __shared__ uint32_t part[kThreads / 64];
+  const bool chan = p.chan_scale != nullptr;
+  const bool had = p.hadamard == 32;
+  const int64_t cpr = p.cols / L;
+  const int64_t total = p.rows * cpr;
+  uint32_t m = 0;
+  // four chunks per thread per pass, all loads issued before the first wait;
+  // whole waves stay in the loop (Hadamard shuffles), and lanes past the end
+  // load the last chunk and do not count it
+  constexpr int U = 4;
+  for (int64_t c0 = 0; c0 < total; c0 += U * kThreads) {
+    Raw<L, BF16> raw[U];
+    int64_t cu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads + threadIdx.x;
+      cu[u] = c < total ? c : -1;
+      const int64_t cc = c < total ? c : total - 1;
+      load_raw<L, BF16>(p, cc / cpr, (cc % cpr) * L, raw[u]);
+      load_t<L, BF16>(chan_view(p), (cc % cpr) * L, raw[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[L];
+      const int64_t cc = cu[u] >= 0 ? cu[u] : total - 1;
+      finish_chunk<L, BF16, true>(p, (cc % cpr) * L, raw[u], x, chan, had);
+      if (cu[u] >= 0)
+#pragma unroll
+        for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t a = part[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) a = max(a, part[w]);
+  const float g = (a == 0u) ? 1.0f : bitsf(a) / p.fused_denom;
+  if (threadIdx.x == 0) *p.global = g;
+  return g;
+}
+
 // CONTIG: rows are contiguous (ld == cols) and there is no channel scale, so
 // the tensor is walked as one row of rows * cols elements
 template <int FMT, int B, int RULE, bool BF16, bool CONTIG>
@@ -606,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   // decisions on the fly
   constexpr bool TABLES = (FMT == RAZER_W || RULE == BRUTE);
   __shared__ Tables<TABLES ? FMT : MXFP4> T;
-  const float g = p.global ? *p.global : 1.0f;
+  const float g = (p.fused_denom > 0.0f) ? fused_auto_global<L, BF16>(p) : (p.global ? *p.global : 1.0f);
   if constexpr (TABLES) {
     build_tables<FMT>(T, g, p.special);
     __syncthreads();
@@ -976,6 +1029,12 @@ __global__ __launch_bounds__(kThreads) void channel_scale_kernel(ChanScaleParams
   }
 }
 
+// automatic g in the quantize launch itself up to this many elements: one
+// pass of four chunks per thread of one workgroup for the maximum (one load
+// latency), which beats three extra launches; larger tensors need more
+// dependent passes than the launches cost
+constexpr int64_t kFusedAutoMax = 8192;
+
 int grid_for(int64_t work_items, int64_t cap = 256 * 16) {  // default: 16 workgroups per CU on 256 CUs
   int64_t blocks = (work_items + kThreads - 1) / kThreads;
   if (blocks > cap) blocks = cap;
@@ -987,7 +1046,7 @@ template <int FMT, int B, int RULE>
 hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   constexpr int L = (B == 4) ? 4 : 8;
   const int64_t chunks = p.rows * (p.cols / L);
-  int grid = grid_for(chunks);
+  int grid = p.fused_denom > 0.0f ? 1 : grid_for(chunks);
   // kernels that build LDS tables per workgroup: a few chunks per thread
   // (2 for small tensors, where the grid is short of the CUs anyway, 4 above)
   if (FMT == RAZER_W || RULE == BRUTE) {
@@ -1023,7 +1082,13 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
                            hipStream_t s) {
   if (p.rows == 0) return hipSuccess;
   const bool bf16 = p.x_bf16 != 0;
-  if (gmode == G_AUTO) {
+  QuantParams q = p;
+  q.fused_denom = 0.0f;
+  const float denom = fmt == RAZER_W ? 180.0f : 2688.0f;
+  if (gmode == G_AUTO && p.rows * p.cols <= kFusedAutoMax) {
+    // small tensor: one workgroup finds g and quantizes, in one launch
+    q.fused_denom = denom;
+  } else if (gmode == G_AUTO) {
     hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
     if (p.cols % 8 == 0) {
       int grid = grid_for(p.rows * (p.cols / 8), 256 * 4);
@@ -1034,19 +1099,18 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
       if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL(amax4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
     }
-    hipLaunchKernelGGL(finalize_global_kernel, dim3(1), dim3(1), 0, s, p.global,
-                       fmt == RAZER_W ? 180.0f : 2688.0f);
+    hipLaunchKernelGGL(finalize_global_kernel, dim3(1), dim3(1), 0, s, p.global, denom);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   switch (fmt) {
-    case MXFP4: return launch_q3<MXFP4, 32, ABSMAX>(bf16, p, s);
-    case RAZER_A: return launch_q2<RAZER_A, ABSMAX>(block, bf16, p, s);
-    case RAZER_W: return launch_q2<RAZER_W, ABSMAX>(block, bf16, p, s);
+    case MXFP4: return launch_q3<MXFP4, 32, ABSMAX>(bf16, q, s);
+    case RAZER_A: return launch_q2<RAZER_A, ABSMAX>(block, bf16, q, s);
+    case RAZER_W: return launch_q2<RAZER_W, ABSMAX>(block, bf16, q, s);
     default:
-      if (rule == FOUR6) return launch_q2<NVFP4, FOUR6>(block, bf16, p, s);
-      if (rule == BRUTE) return launch_q2<NVFP4, BRUTE>(block, bf16, p, s);
-      return launch_q2<NVFP4, ABSMAX>(block, bf16, p, s);
+      if (rule == FOUR6) return launch_q2<NVFP4, FOUR6>(block, bf16, q, s);
+      if (rule == BRUTE) return launch_q2<NVFP4, BRUTE>(block, bf16, q, s);
+      return launch_q2<NVFP4, ABSMAX>(block, bf16, q, s);
   }
 }
 

@@ -225,6 +225,18 @@ def test_mxfp4_linear_workload(B):
     sampled_parity(B, w, dev(w), "mxfp4", 32, "absmax", "none", sample_rows(14336, 64, 21), t=r, had=32)
 
 
+# automatic g on both sides of the single-launch threshold (8192 elements):
+# 1 x 8192 finds g inside the quantize launch, 2 x 4608 with the separate
+# abs-max and finalize launches; codes, scales and g must match the oracle
+@pytest.mark.parametrize("rows,cols", [(1, 8192), (2, 4608), (1, 5120)])
+def test_auto_global_launch_paths(B, rows, cols):
+    x = datagen.student_t((rows, cols), 950 + rows, 3.0)
+    xg = dev(x)
+    t = (datagen.rng(951).random(cols) + 0.5).astype(np.float32)
+    run_pair(B, x, xg, "nvfp4", 16, "4over6", "auto", t=t, had=32)
+    run_pair(B, x, xg, "razer_w", 16, "absmax", "auto", special=SPECIAL)
+
+
 def test_razer_decode_workload(B):
     w = datagen.razer_decode(1)["W"]
     sampled_parity(B, w, dev(w), "razer_w", 16, "absmax", "auto", sample_rows(17408, 64, 30), special=SPECIAL)
