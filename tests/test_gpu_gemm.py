@@ -96,7 +96,8 @@ def test_gemm_decode_shapes(B, fa, fw, M, N, K, out_dtype):
 # group of four 128-element stages): ragged M and N, one group (K = 512),
 # FP32 output with few tiles (K splits rounded to whole groups, some splits
 # left empty) and bf16 output
-@pytest.mark.parametrize("M,N,K", [(300, 260, 1024), (64, 96, 2048), (257, 129, 512), (33, 300, 1536)])
+@pytest.mark.parametrize("M,N,K", [(300, 260, 1024), (64, 96, 2048), (257, 129, 512), (33, 300, 1536),
+                                   (1, 1, 512), (2, 40, 1024), (1, 300, 2560)])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_gemm_mxfp4_group_staging(B, M, N, K, out_dtype):
     a = datagen.student_t((M, K), 920 + M, 4.0)
