@@ -731,47 +731,63 @@ __device__ __forceinline__ void dl_barrier() {
 }
 
 struct DlLoader {
+  // per-lane offsets are recomputed from the thread index at each issue (a
+  // few VALU per pair), so that they hold no registers across the K loop
   __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
-  uint32_t a_off[8], w_off[8];  // this lane's row and chunk offsets in its 8 A and 8 W units
-  uint32_t sa_off, sw_off;      // this thread's scale row
+  uint32_t lastA, lastW;        // last valid row of the A and W panels (rows past it are clamped)
+  uint32_t rowbytes;            // K / 2
+  uint32_t nblocks;             // scale bytes per row
   int wv;                       // wave index (uniform)
 
-  __device__ void init(const GemmParams& p, int64_t m0, int64_t n0) {
+  int blk;                      // elements per scale byte (32 MXFP4, 16 NVFP4 family)
+
+  __device__ void init(const GemmParams& p, int64_t m0, int64_t n0, int block) {
     const int t = threadIdx.x, lane = t & 63;
     wv = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int64_t rowbytes = p.K / 2, nblocks = p.K / 32;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = 8 * (t >> 6) + j, r7 = lane >> 3;
-      const int row = 8 * blk + r7, ch = (lane & 7) ^ ((r7 >> 1) | ((blk & 1) << 2));
-      a_off[j] = (uint32_t)(min((int64_t)row, p.M - 1 - m0) * rowbytes + 16 * ch);
-      w_off[j] = (uint32_t)(min((int64_t)row, p.N - 1 - n0) * rowbytes + 16 * ch);
-    }
-    sa_off = (uint32_t)(min((int64_t)t, p.M - 1 - m0) * nblocks);
-    sw_off = (uint32_t)(min((int64_t)t, p.N - 1 - n0) * nblocks);
-    ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_codes + m0 * rowbytes), (short)0, -1, (int)kRsrcWord3);
-    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + n0 * rowbytes), (short)0, -1, (int)kRsrcWord3);
-    rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_scales + m0 * nblocks), (short)0, -1, (int)kRsrcWord3);
-    rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + n0 * nblocks), (short)0, -1, (int)kRsrcWord3);
+    blk = block;
+    nblocks = (uint32_t)(p.K / block);
+    rowbytes = (uint32_t)(p.K / 2);
+    lastA = (uint32_t)min(p.M - 1 - m0, (int64_t)255);
+    lastW = (uint32_t)min(p.N - 1 - n0, (int64_t)255);
+    (void)lane;
+    ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_codes + m0 * (int64_t)rowbytes), (short)0, -1,
+                                           (int)kRsrcWord3);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + n0 * (int64_t)rowbytes), (short)0, -1,
+                                           (int)kRsrcWord3);
+    rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_scales + m0 * (int64_t)nblocks), (short)0, -1,
+                                            (int)kRsrcWord3);
+    rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + n0 * (int64_t)nblocks), (short)0, -1,
+                                            (int)kRsrcWord3);
   }
 
   // the kDlPairLoads code loads of the pair of stages at k0 into the pair
   // buffer `buf`: blocks 8 wv .. 8 wv + 7 of each operand
+  // (block 8 wv + j: row 8 (8 wv + j) + lane / 8, clamped, chunk bits of the
+  // block's parity; offsets below 2^32: at most 255 rows of K / 2 <= 2^23 bytes)
   __device__ __forceinline__ void issue_pair(uint8_t* buf, int64_t k0) const {
     const int kb = (int)(k0 / 2);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t lrow = 64 * (threadIdx.x >> 6) + (lane >> 3);  // this lane's row in the first block
+    const uint32_t chb = 16 * ((lane & 7) ^ (lane >> 4));          // its chunk in even blocks (odd: ^ 64)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (8 * wv + j) * 1024), 16, a_off[j], kb, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = __umul24(min(lrow + 8 * j, lastA), rowbytes) + (chb ^ ((j & 1) * 64));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(buf + (8 * wv + j) * 1024), 16, off, kb, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (8 * wv + j) * 1024), 16, w_off[j], kb,
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = __umul24(min(lrow + 8 * j, lastW), rowbytes) + (chb ^ ((j & 1) * 64));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(buf + kDlCodes + (8 * wv + j) * 1024), 16, off, kb,
                                                0, 0);
+    }
   }
 
-  // the two scale loads (A, W) of the group of stages starting at k0 into the
-  // group buffer `sbuf`: rows 64 wv + lane, 16 bytes each
+  // the two scale loads (A, W) of 16 bytes of each row from element k0 into
+  // `sbuf`: rows 64 wv + lane, A at 16 row, W at 16 (BM + row)
   __device__ __forceinline__ void issue_scales(uint8_t* sbuf, int64_t k0) const {
-    const int b0 = (int)(k0 / 32);
+    const int b0 = (int)(k0 / blk);
+    const uint32_t sa_off = __umul24(min(threadIdx.x, lastA), nblocks);
+    const uint32_t sw_off = __umul24(min(threadIdx.x, lastW), nblocks);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(sbuf + 1024 * wv), 16, sa_off, b0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr)(sbuf + BM * 16 + 1024 * wv), 16, sw_off, b0, 0, 0);
   }
@@ -901,7 +917,7 @@ __device__ __forceinline__ void dl_prologue(uint8_t* __restrict__ b0, uint8_t* _
 __device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm,
                                            int wn, int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
   DlLoader L;
-  L.init(p, m0, n0);
+  L.init(p, m0, n0, 32);
   const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
   DlAddr ad;
   const int r7 = r32 & 7, x = (r7 >> 1) | (((r32 >> 3) & 1) << 2);
@@ -945,6 +961,219 @@ __device__ __forceinline__ void mx_tile_dl(const GemmParams& p, int64_t m0, int6
                                             ad, r, acc);
 }
 
+// ---------------------------------------------------------------- NVFP4 K loop, LDS-DMA staging
+// NVFP4 family with K % 256 == 0 and 16-byte aligned scale rows: the code
+// layout and loads of the MXFP4 LDS-DMA path (pairs of stages, 128 bytes of
+// each row), plus one 16-byte scale load per row per pair (the pair's 16
+// E4M3/E3M3 bytes, stage h at bytes 8 h .. 8 h + 7) into the pair buffer.
+// Lane (r32, kh) forms its stage scale dword (blocks 2 kh, 2 kh + 1 of chunk
+// 0, 4 + 2 kh, 5 + 2 kh of chunk 1) from the row's 8 stage bytes with one byte
+// permute.  The stage is the register path's: 8 MFMA steps, the decode of
+// step t + 1 during step t, the barrier after step 2, stage s + 1's scales and
+// chunk-0 codes read at step 3 and chunk-1 codes at step 7.
+constexpr int kNvPairBuf = 2 * kDlCodes + 2 * BM * 16;  // 72 KiB: codes + scales of a pair
+constexpr int kNvPairLoads = 18;                        // per wave per pair: 16 code + 2 scale loads
+static_assert(2 * kNvPairBuf <= kDlLds, "two pair buffers fit the ring");
+
+// LDS addresses of the NVFP4 LDS-DMA reads, relative to a pair buffer: the A
+// code fragment of tile 0 for chunk kc of the pair's first stage (the second
+// stage's is that ^ 64: bit 6 is the stage bit of the chunk slot) and the A
+// scale row of tile 0; W's are these plus wave-uniform deltas
+struct NvDlAddr {
+  uint32_t a[2];
+  uint32_t sa;
+  int dw, dsw;
+};
+
+template <int H, int KC>
+__device__ __forceinline__ void nv_dl_read_codes(const uint8_t* buf, const NvDlAddr& ad, uint4 (&ca)[4],
+                                                 uint4 (&cw)[4]) {
+  const uint32_t o = H ? (ad.a[KC] ^ 64u) : ad.a[KC];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ca[i] = *(const uint4*)(buf + o + i * 4096);
+    cw[i] = *(const uint4*)(buf + o + ad.dw + i * 4096);
+  }
+}
+
+// one NVFP4 stage s (half H of its pair).  nxt: the pair buffer of stage s + 1
+// (half HN); ld: where pair (s + 3) / 2 goes (ISSUE: odd s, issued after the
+// barrier; nxt and ld are different buffers, and stage s reads only nxt).
+// WAITN: this wave's loads left in flight at the barrier (the next pair's at
+// even stages, none at odd ones).
+template <int FA, int FW, bool ISSUE, int WAITN, int HN, bool NEXT>
+__device__ __forceinline__ void nv_stage_dl(const uint8_t* __restrict__ nxt, uint8_t* __restrict__ ld,
+                                            const DlLoader& L, int64_t k_ld, const NvDlAddr& ad, uint32_t sel,
+                                            uint32_t sp_lo, uint32_t sp_hi, NvRegs& R, half8 (&da)[2][4],
+                                            half8 (&db)[2][4], f32x16 (&acc)[4][4]) {
+  constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);
+  uint32_t sa8[4][2], sw8[4][2];
+  auto prep_a = [&](auto kc_tag, uint32_t (&pa)[4], uint32_t (&xa)[4]) {
+    constexpr int KC = decltype(kc_tag)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = scale_pair_f16<FA, KC>(R.ra[i]);
+      if constexpr (RZ) xa[i] = special_pair_f16<FA, KC>(R.ra[i], pa[i], sp_lo, sp_hi);
+    }
+  };
+  auto prep_w = [&](auto kc_tag, uint32_t (&pw)[4], uint32_t (&xw)[4]) {
+    constexpr int KC = decltype(kc_tag)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = scale_pair_f16<FW, KC>(R.rw[i]);
+      if constexpr (RZ) xw[i] = special_pair_f16<FW, KC>(R.rw[i], pw[i], sp_lo, sp_hi);
+    }
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  static_for<0, 8>([&](auto tc) {
+    constexpr int t = decltype(tc)::value, cur = t & 1;
+    if constexpr (t == 0) prep_a(K1{}, R.pa1, R.xa1);  // chunk-1 pairs, A at step 0, W at step 1
+    if constexpr (t == 1) prep_w(K1{}, R.pw1, R.xw1);
+    if constexpr (t == 3) {
+      if constexpr (ISSUE) {
+        L.issue_pair(ld, k_ld);
+        L.issue_scales(ld + 2 * kDlCodes, k_ld);
+      }
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint2 va = *(const uint2*)(nxt + ad.sa + i * 512 + 8 * HN);
+          const uint2 vw = *(const uint2*)(nxt + ad.sa + ad.dsw + i * 512 + 8 * HN);
+          sa8[i][0] = va.x; sa8[i][1] = va.y;
+          sw8[i][0] = vw.x; sw8[i][1] = vw.y;
+        }
+        nv_dl_read_codes<HN, 0>(nxt, ad, R.ca0, R.cw0);
+      }
+    }
+    if constexpr (t == 4 && NEXT) prep_a(K0{}, R.pa0, R.xa0);  // next stage's chunk-0 pairs
+    if constexpr (t == 5 && NEXT) prep_w(K0{}, R.pw0, R.xw0);
+    if constexpr (t == 7 && NEXT) nv_dl_read_codes<HN, 1>(nxt, ad, R.ca1, R.cw1);
+    // decode of step t + 1
+    if constexpr (t < 3)
+      decode_step<FA, FW, t + 1>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[cur ^ 1], db[cur ^ 1]);
+    else if constexpr (t < 7)
+      decode_step<FA, FW, t - 3>(R.ca1, R.cw1, R.pa1, R.pw1, R.xa1, R.xw1, da[cur ^ 1], db[cur ^ 1]);
+    else if constexpr (NEXT)
+      decode_step<FA, FW, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[cur ^ 1], db[cur ^ 1]);
+    mfma_step(da[cur], db[cur], acc);
+    constexpr int nvm = (t == 3 && ISSUE) ? 16 : 0;
+    constexpr int ndsr = (t == 3 && NEXT) ? 16 : (t == 7 && NEXT) ? 8 : 0;
+    constexpr int extra = (t == 0 || t == 1 || t == 4 || t == 5) ? 5 : 4;
+    sched_step<0, nvm, ndsr, extra>();
+    if constexpr (t == 2) dl_barrier<WAITN>();
+    if constexpr (t == 3 && NEXT) {
+      const uint32_t sl = 0x05040100u + ((threadIdx.x >> 5) & 1u) * 0x02020202u;  // bytes 2 kh, 2 kh + 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        R.ra[i] = __builtin_amdgcn_perm(sa8[i][1], sa8[i][0], sl);
+        R.rw[i] = __builtin_amdgcn_perm(sw8[i][1], sw8[i][0], sl);
+      }
+    }
+  });
+}
+
+// pairs 0 and 1, then stage 0's scales and codes once pair 0 has landed
+template <int FA, int FW, bool TWO>
+__device__ __forceinline__ void nv_prologue_dl(uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, const DlLoader& L,
+                                               int64_t kb, const NvDlAddr& ad, uint32_t sel, NvRegs& R) {
+  L.issue_pair(b0, kb);
+  L.issue_scales(b0 + 2 * kDlCodes, kb);
+  if constexpr (TWO) {
+    L.issue_pair(b1, kb + 2 * BK);
+    L.issue_scales(b1 + 2 * kDlCodes, kb + 2 * BK);
+  }
+  dl_barrier<TWO ? kNvPairLoads : 0>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint2 va = *(const uint2*)(b0 + ad.sa + i * 512);
+    const uint2 vw = *(const uint2*)(b0 + ad.sa + ad.dsw + i * 512);
+    R.ra[i] = __builtin_amdgcn_perm(va.y, va.x, sel);
+    R.rw[i] = __builtin_amdgcn_perm(vw.y, vw.x, sel);
+  }
+  nv_dl_read_codes<0, 0>(b0, ad, R.ca0, R.cw0);
+  nv_dl_read_codes<0, 1>(b0, ad, R.ca1, R.cw1);
+}
+
+// four stages 4g .. 4g + 3 with the pair buffers fixed: B0 holds pairs 2g and
+// 2g + 2, B1 pairs 2g + 1 and 2g + 3; k2 is pair 2g + 2's first element.  B0
+// and B1 are distinct, so the compiler orders each LDS read only after the
+// loads into its own buffer, which the odd stages' waits complete.
+template <int FA, int FW>
+__device__ __forceinline__ void nv_group_dl(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, const DlLoader& L,
+                                            int64_t k2, const NvDlAddr& ad, uint32_t sel, uint32_t sp_lo,
+                                            uint32_t sp_hi, NvRegs& R, half8 (&da)[2][4], half8 (&db)[2][4],
+                                            f32x16 (&acc)[4][4]) {
+  nv_stage_dl<FA, FW, false, kNvPairLoads, 1, true>(B0, B1, L, 0, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+  nv_stage_dl<FA, FW, true, 0, 0, true>(B1, B0, L, k2, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+  nv_stage_dl<FA, FW, false, kNvPairLoads, 1, true>(B1, B0, L, 0, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+  nv_stage_dl<FA, FW, true, 0, 0, true>(B0, B1, L, k2 + 2 * BK, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+}
+
+// ns = send - sbeg is a positive multiple of 2 (whole pairs).  Loads in
+// flight per wave: pair q + 1 is issued at odd stage 2 q - 1 (after its
+// barrier); stage s + 1 must have landed at stage s's barrier, which leaves
+// the next pair in flight at even stages and nothing at odd ones.
+template <int FA, int FW>
+__device__ __forceinline__ void nv_tile_dl(const GemmParams& p, int64_t m0, int64_t n0, uint8_t* smem, int wm,
+                                           int wn, int64_t sbeg, int64_t send, f32x16 (&acc)[4][4]) {
+  constexpr bool RZ = (FA == RAZER_A || FW == RAZER_A || FW == RAZER_W);
+  DlLoader L;
+  L.init(p, m0, n0, 16);
+  const int lane = threadIdx.x & 63, r32 = lane & 31, kh = lane >> 5;
+  NvDlAddr ad;
+  const int r7 = r32 & 7, x = (r7 >> 1) | (((r32 >> 3) & 1) << 2);
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+    ad.a[kc] = (uint32_t)((r32 >> 3) * 1024 + 128 * r7 + 16 * ((2 * kc + kh) ^ x) + wm * 16 * 1024);
+  ad.sa = (uint32_t)(2 * kDlCodes + (wm * 128 + r32) * 16);
+  ad.dw = __builtin_amdgcn_readfirstlane(kDlCodes + (wn - wm) * 16 * 1024);
+  ad.dsw = __builtin_amdgcn_readfirstlane(BM * 16 + (wn - wm) * 128 * 16);
+  const uint32_t sel = kh ? 0x07060302u : 0x05040100u;  // bytes 2 kh, 2 kh + 1 of each half
+  const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
+  const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
+  auto pbuf = [&](int64_t pr) { return smem + (int)(pr & 1) * kNvPairBuf; };
+  const int64_t kb = sbeg * BK, ns = send - sbeg, np = ns / 2;
+  NvRegs R;
+  if (np > 1) nv_prologue_dl<FA, FW, true>(pbuf(0), pbuf(1), L, kb, ad, sel, R);
+  else nv_prologue_dl<FA, FW, false>(pbuf(0), pbuf(1), L, kb, ad, sel, R);
+  // the chunk-0 pairs and step-0 decode of stage 0
+  using K0 = std::integral_constant<int, 0>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
+    R.pw0[i] = scale_pair_f16<FW, 0>(R.rw[i]);
+    if constexpr (RZ) {
+      R.xa0[i] = special_pair_f16<FA, 0>(R.ra[i], R.pa0[i], sp_lo, sp_hi);
+      R.xw0[i] = special_pair_f16<FW, 0>(R.rw[i], R.pw0[i], sp_lo, sp_hi);
+    }
+  }
+  half8 da[2][4], db[2][4];
+  decode_step<FA, FW, 0>(R.ca0, R.cw0, R.pa0, R.pw0, R.xa0, R.xw0, da[0], db[0]);
+  // groups of two pairs with the buffers fixed (pair 2g in B0, 2g + 1 in B1):
+  // the odd stages load pairs 2g + 2 (into B0) and 2g + 3 (into B1)
+  int64_t q = 0;
+  for (; q + 3 < np; q += 2)
+    nv_group_dl<FA, FW>(pbuf(0), pbuf(1), L, kb + (2 * q + 4) * BK, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+  // the last one to three pairs (pair r in buffer r % 2), sequenced without
+  // alternatives so that register allocation stays as in the loop
+  if (np - q == 3) {  // pair q + 2 is still to load
+    nv_stage_dl<FA, FW, false, kNvPairLoads, 1, true>(pbuf(q), pbuf(q + 1), L, 0, ad, sel, sp_lo, sp_hi, R, da, db,
+                                                       acc);
+    nv_stage_dl<FA, FW, true, 0, 0, true>(pbuf(q + 1), pbuf(q), L, kb + (2 * q + 4) * BK, ad, sel, sp_lo, sp_hi, R,
+                                          da, db, acc);
+    ++q;
+  }
+  if (np - q == 2) {
+    nv_stage_dl<FA, FW, false, kNvPairLoads, 1, true>(pbuf(q), pbuf(q + 1), L, 0, ad, sel, sp_lo, sp_hi, R, da, db,
+                                                       acc);
+    nv_stage_dl<FA, FW, false, 0, 0, true>(pbuf(q + 1), pbuf(q), L, 0, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+    ++q;
+  }
+  nv_stage_dl<FA, FW, false, kNvPairLoads, 1, true>(pbuf(q), pbuf(q + 1), L, 0, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+  nv_stage_dl<FA, FW, false, 0, 0, false>(pbuf(q + 1), pbuf(q), L, 0, ad, sel, sp_lo, sp_hi, R, da, db, acc);
+}
+
 // ---------------------------------------------------------------- kernel
 // FA, FW: operand formats; FA == MXFP4 selects the block-scaled FP4 MFMA path
 template <int FA, int FW, bool OUT_BF16>
@@ -952,18 +1181,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_tile_kernel(GemmParams p) {
   constexpr bool MX = (FA == MXFP4);
   static_assert(kNbuf * kBufBytes <= kDlLds, "the register-staged layout fits the LDS-DMA ring");
-  __shared__ __align__(16) uint8_t smem[MX ? kDlLds : kNbuf * kBufBytes];
+  __shared__ __align__(16) uint8_t smem[kDlLds];
   // workgroup = (tile, K-split); split s owns stages [s * per, (s + 1) * per)
   const int split = (int)(blockIdx.x % (unsigned)p.splits);
   int tm, tn;
   tile_coords(p.M, p.N, (int)(blockIdx.x / (unsigned)p.splits), tm, tn);
-  // the MXFP4 LDS-DMA path takes whole groups of kDlGroup stages per split
-  const bool dl = MX && p.K % (kDlGroup * BK) == 0 &&
+  // the LDS-DMA paths take whole groups of stages per split: four (MXFP4
+  // scale groups) or two (NVFP4 family pairs)
+  constexpr int DLG = MX ? kDlGroup : 2;
+  const bool dl = p.K % (DLG * BK) == 0 &&
                   ((((uintptr_t)p.a_codes | (uintptr_t)p.w_codes | (uintptr_t)p.a_scales | (uintptr_t)p.w_scales) &
                     15) == 0);
   const int64_t nst = (p.K + BK - 1) / BK;
   int64_t per = (nst + p.splits - 1) / p.splits;
-  if (dl) per = (per + kDlGroup - 1) / kDlGroup * kDlGroup;
+  if (dl) per = (per + DLG - 1) / DLG * DLG;
   const int64_t sbeg = min(nst, split * per), send = min(nst, sbeg + per);
   if (sbeg >= send) return;  // no stages left for this split (uniform across the workgroup)
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -976,8 +1207,10 @@ void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-  if constexpr (!MX) nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
-  else if (dl) mx_tile_dl(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+  if constexpr (!MX) {
+    if (dl) nv_tile_dl<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+    else nv_tile<FA, FW>(p, m0, n0, smem, wm, wn, sbeg, send, acc);
+  } else if (dl) mx_tile_dl(p, m0, n0, smem, wm, wn, sbeg, send, acc);
   else mx_tile(p, m0, n0, smem, wm, wn, sbeg, send, acc);
 
   const float ga = p.a_global ? *p.a_global : 1.0f;
