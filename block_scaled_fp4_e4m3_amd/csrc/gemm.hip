@@ -11,13 +11,14 @@
 //
 // Tiling.  A workgroup of 4 waves computes a 256 x 256 tile; each wave owns a
 // 128 x 128 sub-tile as 4 x 4 MFMA 32x32 accumulators (256 FP32 per lane, in
-// the accumulation registers).  K advances in stages of 128 elements: the
-// packed codes (64 bytes per row) and scale bytes of both operands are loaded
-// with 16-byte buffer loads into registers and written to one of two LDS
-// stage buffers in MFMA fragment order (below), so that every fragment read
-// is one lane-contiguous ds_read_b128.  Workgroup ids are remapped so that
-// each XCD works on a contiguous, grouped range of tiles and its L2 sees
-// shared operand panels.
+// the accumulation registers).  K advances in stages of 128 elements.  When K
+// and the operand alignment allow (K % 256 == 0, or 512 for MXFP4), global
+// loads write the packed codes and scale bytes straight into LDS (LDS-DMA),
+// two stages of each row per load; otherwise 16-byte buffer loads bring them
+// into registers, which are written to one of two LDS stage buffers in MFMA
+// fragment order (below), so that every fragment read is one ds_read_b128.
+// Workgroup ids are remapped so that each XCD works on a contiguous, grouped
+// range of tiles and its L2 sees shared operand panels.
 //
 // MXFP4: codes and E8M0 exponents go straight into the block-scaled FP4 MFMA
 // (V_MFMA_SCALE_F32_32X32X64_F8F6F4); a lane supplies the 32 codes of one MX
