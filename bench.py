@@ -98,6 +98,7 @@ class Prefill:
         self.quantize_call()
         if ev: ev.mark("q1")
         for i, (wc, ws, wg, out) in enumerate(self.w):
+            if ev: ev.mark(f"g{i}s")
             B.gemm("nvfp4", self.codes, self.scales, self.g_act, "nvfp4", wc, ws, wg, out=out)
             if ev: ev.mark(f"g{i}")
 
@@ -141,6 +142,7 @@ class MxLinear:
         if ev: ev.mark("q0")
         self.quantize_call()
         if ev: ev.mark("q1")
+        if ev: ev.mark("g0s")
         B.gemm("mxfp4", self.codes, self.scales, None, "mxfp4", self.wc, self.ws, None, out=self.out)
         if ev: ev.mark("g0")
 
@@ -218,6 +220,7 @@ class RazerDecode:
         if ev: ev.mark("q0")
         self.quantize_call()
         if ev: ev.mark("q1")
+        if ev: ev.mark("g0s")
         B.gemm("razer_a", self.codes, self.scales, self.g, "razer_w", self.wc, self.ws, self.wg, self.sp, out=self.out)
         if ev: ev.mark("g0")
 
@@ -262,12 +265,13 @@ class Marks:
         self.rec.append((name, e))
 
     def durations(self):
-        """ms between consecutive marks: quantize = q0->q1, gemm i = prev->g{i}"""
+        """ms between a mark and the next: quantize = q0 -> q1, gemm i = g{i}s -> g{i}
+        (the start mark sits right before the launch, so a wait for the host
+        to enqueue the GEMM after a short quantize is not counted)"""
         out = {}
         for (n0, e0), (n1, e1) in zip(self.rec, self.rec[1:]):
-            if n1 == "q0":
-                continue
-            out.setdefault(n1, []).append(e0.elapsed_time(e1))
+            if (n0, n1) == ("q0", "q1") or (n0.endswith("s") and n1 == n0[:-1]):
+                out.setdefault(n1, []).append(e0.elapsed_time(e1))
         return out
 
 
