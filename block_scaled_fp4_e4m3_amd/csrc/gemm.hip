@@ -847,14 +847,14 @@ __device__ __forceinline__ void dl_read_codes(const uint8_t* buf, const DlAddr& 
 
 // One stage s, half H of its pair.  cur: the pair buffer of stage s; nxt:
 // that of stage s + 1 (half HN); ld: where the code loads of pair (s + 3) / 2
-// go (ISSUE, odd s: the buffer of stage s's pair, whose last read is this
-// stage's step 0); srd: the scale group buffer of stage s + 1, whose dwords
-// sit at phase PHN; sld: where the next group's scales go (SCALES).  The
-// accesses through these pointers that `__restrict__` declares disjoint are:
-// the code loads into ld and the reads of nxt, srd; the scale loads into sld
-// and the reads of srd, nxt.  The reads of cur come before the barrier, the
-// loads after it.  WAITN: this wave's loads left in flight when stage s + 1's
-// codes and scales must have landed.
+// go (ISSUE, odd s: the buffer of stage s's own pair, whose last read is this
+// stage's step 0; that read then goes through ld too, so that no buffer is
+// reached through two of the `__restrict__` pointers); srd: the scale group
+// buffer of stage s + 1, whose dwords sit at phase PHN; sld: where the next
+// group's scales go (SCALES).  The buffers accessed through different
+// pointers are distinct, so the compiler orders each LDS read only after the
+// loads into its own buffer.  WAITN: this wave's loads left in flight when
+// stage s + 1's codes and scales must have landed.
 //   step 0: read stage s's chunk-1 codes, shift stage s's scale dwords, chunk
 //           0 x tiles 0-1;
 //   step 1: chunk 0 x tiles 2-3; wait; barrier;
@@ -867,7 +867,8 @@ __device__ __forceinline__ void dl_stage(const uint8_t* __restrict__ cur, const 
                                          uint8_t* __restrict__ ld, const uint8_t* __restrict__ srd,
                                          uint8_t* __restrict__ sld, const DlLoader& L, int64_t k_ld, int64_t k_sc,
                                          const DlAddr& ad, DlRegs& r, f32x16 (&acc)[4][4]) {
-  dl_read_codes<H, 1>(cur, ad, r.ca1, r.cw1);
+  if constexpr (ISSUE) dl_read_codes<H, 1>(ld, ad, r.ca1, r.cw1);  // ld is stage s's buffer
+  else dl_read_codes<H, 1>(cur, ad, r.ca1, r.cw1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     r.sa[i] >>= ad.sh;
