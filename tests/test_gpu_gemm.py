@@ -111,6 +111,28 @@ def test_gemm_mxfp4_group_staging(B, M, N, K, out_dtype):
     assert rel_fro(got, ref) <= tol
 
 
+# NVFP4-family shapes with K % 256 == 0 and M > 128 (the tile kernel's
+# LDS-DMA staging in pairs of stages): 2, 3, 5 and 7 pairs cover the tail
+# variants (one to three pairs after the four-stage main loop, with and
+# without a load in the tail); FP32 output on two tiles also splits K into
+# pair-aligned ranges
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w")])
+@pytest.mark.parametrize("K", [512, 768, 1280, 1792])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_nvfp4_pair_staging(B, fa, fw, K, out_dtype):
+    M, N = 200, 300
+    a = datagen.student_t((M, K), 960 + K, 4.0)
+    w = datagen.normal((N, K), 961 + K, 0.02)
+    sp = SPECIAL if fw == "razer_w" else None
+    ca, sa, ga = oquant(a, fa)
+    cw, sw, gw = oquant(w, fw, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, M, N, K)
+    case(f"gemm pair staging {fa}x{fw} {M}x{N}x{K} {out_dtype}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp, out_dtype)
+    tol = TOL if out_dtype == "f32" else 8e-3
+    assert rel_fro(got, ref) <= tol
+
+
 # scale rows at any byte alignment (only codes and C must be 16-byte aligned):
 # 16-byte aligned scales take the MXFP4 LDS-DMA path when K % 512 == 0, word
 # aligned ones the register path with word loads, others byte loads
