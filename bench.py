@@ -378,7 +378,7 @@ def summarize_stats(stats_csv: str, out_md: str, title: str, command: str) -> No
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     with open(out_md, "w") as f:
-        f.write(f"# {title}\n\nCommand (from the repository root on the GPU box):\n\n```\n{command}\n```\n\n")
+        f.write(f"# {title}\n\nCommand (from the repository root, on an MI355X):\n\n```\n{command}\n```\n\n")
         f.write("| kernel | calls | average (us) | min (us) | max (us) | share (%) |\n|---|---|---|---|---|---|\n")
         for r in rows:
             name = r["Name"].replace("fp4q::(anonymous namespace)::", "").replace("void ", "")
@@ -443,8 +443,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: libfp4q has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -58,7 +58,7 @@ typedef enum {
   FP4Q_ERR_ALIGN = 3,       /* pointer or row pitch not 16-byte aligned         */
   FP4Q_ERR_FORMAT = 4,      /* unknown format, or a format pair not supported   */
   FP4Q_ERR_ARG = 5,         /* bad rule, mode, block, transform or special value */
-  FP4Q_ERR_UNSUPPORTED = 6, /* valid combination not implemented by this build  */
+  FP4Q_ERR_UNSUPPORTED = 6, /* valid combination not implemented by libfp4q   */
   FP4Q_ERR_DEVICE = 7       /* the HIP runtime reported an error                */
 } fp4q_status;
 

@@ -41,7 +41,7 @@ def test_e8m0_decode_matches_torch():
 
 def test_e3m3_six_bit_format():
     # RaZeR summary 2.1: a 6-bit scale for weights (64 codes).  Bias 3 with
-    # subnormals is this build's reading: 64 distinct non-negative values,
+    # subnormals is the reading taken here: 64 distinct non-negative values,
     # strictly increasing, 8 per binade with uniform spacing, max 30, min 2^-5.
     v = [O.e3m3_value(k) for k in range(64)]
     assert v[0] == 0 and all(b > a for a, b in zip(v, v[1:]))
