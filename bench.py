@@ -373,6 +373,38 @@ def copy_probe():
     log("[bench] copy probe done")
 
 
+def quant_sweep() -> dict:
+    """NVFP4 quantizer over a 4096 x 4096 FP32 tensor of normal samples, for
+    abs-max, prevent-zero and 4-over-6 at block sizes 4, 8, 16 and 32
+    ([Finer] Method 2).  Each case is timed by graph replay, once with a given
+    global scale (one pass over the input) and once with the automatic one
+    (abs-max pass, finalize and zeroing launches added).  Algorithmic bytes per
+    launch: the FP32 input, half a byte of codes and 1/B byte of scale per
+    element."""
+    import torch
+    import datagen
+    import block_scaled_fp4_e4m3_amd as B
+    x_np = datagen.sweep("normal")
+    R, C = x_np.shape
+    x = torch.from_numpy(x_np).to("cuda")
+    g = torch.full((1,), float(np.abs(x_np).max()) / 2688.0, device="cuda")
+    ga = torch.empty(1, device="cuda")
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+    cases = []
+    for rule in ("absmax", "absmax+pz", "4over6"):
+        for blk in (4, 8, 16, 32):
+            scales = torch.empty((R, C // blk), dtype=torch.uint8, device="cuda")
+            t = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "given", global_=g, codes=codes, scales=scales))
+            ta = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "auto", global_=ga, codes=codes, scales=scales))
+            nbytes = R * C * 4 + R * C // 2 + R * C // blk
+            cases.append({"rule": rule, "block": blk, "given_us": round(t, 2), "bytes": nbytes,
+                          "GB/s": round(nbytes / t / 1e3, 1), "frac_hbm": round(nbytes / t / 1e3 / 8000.0, 4),
+                          "auto_us": round(ta, 2)})
+            log(f"[sweep] {rule} B={blk}: {t:.1f} us given, {ta:.1f} us auto")
+    return {"workload": f"nvfp4_quantize_sweep_{R}x{C}_f32_normal", "timing": "graph replay",
+            "peak_GB/s": 8000.0, "cases": cases}
+
+
 def summarize_stats(stats_csv: str, out_md: str, title: str, command: str) -> None:
     """rocprofv3 kernel_stats.csv -> short markdown table"""
     import csv
@@ -425,6 +457,8 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-scaling copy kernel and exit")
+    ap.add_argument("--quant-sweep", action="store_true",
+                    help="time the NVFP4 quantizer over rules x block sizes on 4096 x 4096 FP32, print one JSON line, exit")
     ap.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--traffic-record", nargs=5,
@@ -453,6 +487,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.quant_sweep:
+        print(json.dumps(quant_sweep()))
         return
 
     wl = WORKLOADS[args.workload](B)
