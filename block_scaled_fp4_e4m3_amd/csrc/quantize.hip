@@ -497,6 +497,24 @@ __device__ __forceinline__ uint32_t resolve_codes(const float* x, uint32_t plo, 
   return (plo & ~up) | (((inc & 0x77777777u) | (plo & 0x88888888u)) & up);
 }
 
+// NVFP4 codes by the exact threshold search (a wave with a non-finite block,
+// or s g near the ends of the FP32 range).  Kept out of line: inlined, its
+// 7 x L comparison masks claim the scalar registers of the whole kernel.
+template <int L>
+__device__ __attribute__((noinline)) uint32_t encode_nv_thresholds(float __attribute__((ext_vector_type(L))) x, int k,
+                                                                   float g) {
+  uint32_t t[7];
+  nv_thresholds(k, (double)g, t);
+  uint32_t plo = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const uint32_t b = fbits(x[i]);
+    const int m = rtn_count(b & 0x7FFFFFFFu, t);
+    plo |= (m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u) << (4 * i);
+  }
+  return plo;
+}
+
 // NVFP4 codes of a lane's L elements for scale code k (value s) under global
 // g: bracketed convert; when some element of the wave cannot be decided that
 // way (on or near a midpoint), the whole wave resolves its elements exactly
@@ -532,16 +550,11 @@ __device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, fl
         amb &= ~(0xFu << sh);
       }
     } else {
-      uint32_t t[7];
-      nv_thresholds(k, (double)g, t);
-      plo = 0;
+      typedef float fLv __attribute__((ext_vector_type(L)));
+      fLv xv;
 #pragma unroll
-      for (int i = 0; i < L; ++i) {
-        const uint32_t b = fbits(x[i]);
-        const int m = rtn_count(b & 0x7FFFFFFFu, t);
-        plo |= (m ? ((uint32_t)m | ((b >> 28) & 8u)) : 0u) << (4 * i);
-      }
-      return plo;
+      for (int i = 0; i < L; ++i) xv[i] = x[i];
+      return encode_nv_thresholds<L>(xv, k, g);
     }
   }
   return clear_neg_zero(plo);
