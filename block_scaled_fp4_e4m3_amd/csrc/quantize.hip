@@ -497,6 +497,24 @@ __device__ __forceinline__ uint32_t resolve_codes(const float* x, uint32_t plo, 
   return (plo & ~up) | (((inc & 0x77777777u) | (plo & 0x88888888u)) & up);
 }
 
+// MXFP4 codes by the exact threshold search (a wave with a non-finite block,
+// or a shared exponent below the normal range): thresholds 2^E times the E2M1
+// midpoints (exact), as bit patterns, strict > for the even ones and >= (one
+// below) for the odd ones (ties to even).  Out of line for the same reason as
+// the NVFP4 search below.
+template <int L>
+__device__ __attribute__((noinline)) uint32_t encode_mx_thresholds(float __attribute__((ext_vector_type(L))) xv,
+                                                                   int E) {
+  float x[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) x[i] = xv[i];
+  const uint32_t t0 = fbits(ldexpf(kMid[0], E)), t1 = fbits(ldexpf(kMid[1], E)) - 1u;
+  const uint32_t t2 = fbits(ldexpf(kMid[2], E)), t3 = fbits(ldexpf(kMid[3], E)) - 1u;
+  const uint32_t t4 = fbits(ldexpf(kMid[4], E)), t5 = fbits(ldexpf(kMid[5], E)) - 1u;
+  const uint32_t t6 = fbits(ldexpf(kMid[6], E));
+  return encode_plain_v<L>(x, t0, t1, t2, t3, t4, t5, t6);
+}
+
 // NVFP4 codes by the exact threshold search (a wave with a non-finite block,
 // or s g near the ends of the FP32 range).  Kept out of line: inlined, its
 // 7 x L comparison masks claim the scalar registers of the whole kernel.
@@ -763,13 +781,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         });
         packed = clear_neg_zero(packed);
       } else {
-        // thresholds 2^E x midpoints (exact), as bit patterns: strict > for
-        // the even ones, >= (one below) for the odd ones (ties to even)
-        const uint32_t t0 = fbits(ldexpf(kMid[0], E)), t1 = fbits(ldexpf(kMid[1], E)) - 1u;
-        const uint32_t t2 = fbits(ldexpf(kMid[2], E)), t3 = fbits(ldexpf(kMid[3], E)) - 1u;
-        const uint32_t t4 = fbits(ldexpf(kMid[4], E)), t5 = fbits(ldexpf(kMid[5], E)) - 1u;
-        const uint32_t t6 = fbits(ldexpf(kMid[6], E));
-        packed = encode_plain_v<L>(x, t0, t1, t2, t3, t4, t5, t6);
+        typedef float fLv __attribute__((ext_vector_type(L)));
+        fLv xv;
+#pragma unroll
+        for (int i = 0; i < L; ++i) xv[i] = x[i];
+        packed = encode_mx_thresholds<L>(xv, E);
       }
       sbyte = (uint8_t)(E + 127);
     } else if constexpr (FMT == NVFP4) {
