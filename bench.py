@@ -374,35 +374,40 @@ def copy_probe():
 
 
 def quant_sweep() -> dict:
-    """NVFP4 quantizer over a 4096 x 4096 FP32 tensor of normal samples, for
-    abs-max, prevent-zero and 4-over-6 at block sizes 4, 8, 16 and 32
-    ([Finer] Method 2).  Each case is timed by graph replay, once with a given
-    global scale (one pass over the input) and once with the automatic one
-    (abs-max pass, finalize and zeroing launches added).  Algorithmic bytes per
-    launch: the FP32 input, half a byte of codes and 1/B byte of scale per
+    """NVFP4 quantizer over 4096 x 4096 FP32 tensors (normal samples, and a
+    heavy-tailed Student-t with 3 degrees of freedom), for abs-max,
+    prevent-zero, 4-over-6 and the brute-force search at block sizes 4, 8, 16
+    and 32 ([Finer] Method 2).  Each case is timed by graph replay, once with
+    a given global scale (one pass over the input) and once with the automatic
+    one (abs-max pass, finalize and zeroing launches added).  Algorithmic bytes
+    per launch: the FP32 input, half a byte of codes and 1/B byte of scale per
     element."""
     import torch
     import datagen
     import block_scaled_fp4_e4m3_amd as B
-    x_np = datagen.sweep("normal")
-    R, C = x_np.shape
-    x = torch.from_numpy(x_np).to("cuda")
-    g = torch.full((1,), float(np.abs(x_np).max()) / 2688.0, device="cuda")
-    ga = torch.empty(1, device="cuda")
-    codes = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
-    cases = []
-    for rule in ("absmax", "absmax+pz", "4over6"):
-        for blk in (4, 8, 16, 32):
-            scales = torch.empty((R, C // blk), dtype=torch.uint8, device="cuda")
-            t = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "given", global_=g, codes=codes, scales=scales))
-            ta = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "auto", global_=ga, codes=codes, scales=scales))
-            nbytes = R * C * 4 + R * C // 2 + R * C // blk
-            cases.append({"rule": rule, "block": blk, "given_us": round(t, 2), "bytes": nbytes,
-                          "GB/s": round(nbytes / t / 1e3, 1), "frac_hbm": round(nbytes / t / 1e3 / 8000.0, 4),
-                          "auto_us": round(ta, 2)})
-            log(f"[sweep] {rule} B={blk}: {t:.1f} us given, {ta:.1f} us auto")
-    return {"workload": f"nvfp4_quantize_sweep_{R}x{C}_f32_normal", "timing": "graph replay",
-            "peak_GB/s": 8000.0, "cases": cases}
+    out = {"workload": "nvfp4_quantize_sweep_4096x4096_f32", "timing": "graph replay",
+           "peak_GB/s": 8000.0, "cases": []}
+    for dist in ("normal", "student_t3"):
+        x_np = datagen.sweep(dist)
+        R, C = x_np.shape
+        x = torch.from_numpy(x_np).to("cuda")
+        g = torch.full((1,), float(np.abs(x_np).max()) / 2688.0, device="cuda")
+        ga = torch.empty(1, device="cuda")
+        codes = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+        for rule in ("absmax", "absmax+pz", "4over6", "brute"):
+            for blk in (4, 8, 16, 32):
+                scales = torch.empty((R, C // blk), dtype=torch.uint8, device="cuda")
+                t = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "given", global_=g, codes=codes,
+                                                scales=scales))
+                ta = graph_us(lambda: B.quantize(x, "nvfp4", blk, rule, "auto", global_=ga, codes=codes,
+                                                 scales=scales))
+                nbytes = R * C * 4 + R * C // 2 + R * C // blk
+                out["cases"].append({"dist": dist, "rule": rule, "block": blk, "given_us": round(t, 2),
+                                     "bytes": nbytes, "GB/s": round(nbytes / t / 1e3, 1),
+                                     "frac_hbm": round(nbytes / t / 1e3 / 8000.0, 4), "auto_us": round(ta, 2)})
+                log(f"[sweep] {dist} {rule} B={blk}: {t:.1f} us given, {ta:.1f} us auto")
+        del x, codes
+    return out
 
 
 def summarize_stats(stats_csv: str, out_md: str, title: str, command: str) -> None:
