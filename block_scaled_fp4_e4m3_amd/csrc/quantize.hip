@@ -1028,29 +1028,42 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantParams p) {
 }
 
 // ---------------------------------------------------------------- channel scale
-// MACaQ section 3: t_j = (rms_j(W) / rms_j(X))^alpha; 64 columns per
-// workgroup, 4 row slices combined in a fixed order
+// MACaQ section 3: t_j = (rms_j(W) / rms_j(X))^alpha.  A workgroup owns 16
+// columns, so that a 4096-column calibration fills 256 CUs: thread (slice y,
+// column x) sums the squares of rows y, y + 64, ... in binary64 (a wave reads
+// 4 rows of its 16 columns per step), then the 64 row slices of a column
+// combine in a fixed pairwise order.
+constexpr int kCsThreads = 1024, kCsCols = 16, kCsSlices = kCsThreads / kCsCols;
+
 __device__ __forceinline__ double load_any(const void* base, int bf16, int64_t idx) {
   if (bf16) return (double)bitsf((uint32_t)((const uint16_t*)base)[idx] << 16);
   return (double)((const float*)base)[idx];
 }
 
-__global__ __launch_bounds__(kThreads) void channel_scale_kernel(ChanScaleParams p) {
-  __shared__ double part[2][4][64];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 64 + tx;
+__global__ __launch_bounds__(kCsThreads) void channel_scale_kernel(ChanScaleParams p) {
+  __shared__ double part[2][kCsSlices][kCsCols];
+  const int tx = threadIdx.x % kCsCols, ty = threadIdx.x / kCsCols;
+  const int64_t j = (int64_t)blockIdx.x * kCsCols + tx;
   double sx = 0.0, sw = 0.0;
   if (j < p.cols) {
-    for (int64_t i = ty; i < p.rows_x; i += 4) { double v = load_any(p.x, p.x_bf16, i * p.ldx + j); sx += v * v; }
-    for (int64_t i = ty; i < p.rows_w; i += 4) { double v = load_any(p.w, p.w_bf16, i * p.ldw + j); sw += v * v; }
+#pragma unroll 4
+    for (int64_t i = ty; i < p.rows_x; i += kCsSlices) { double v = load_any(p.x, p.x_bf16, i * p.ldx + j); sx += v * v; }
+#pragma unroll 4
+    for (int64_t i = ty; i < p.rows_w; i += kCsSlices) { double v = load_any(p.w, p.w_bf16, i * p.ldw + j); sw += v * v; }
   }
   part[0][ty][tx] = sx;
   part[1][ty][tx] = sw;
+  // pairwise tree over the slices: level h adds slice k + h into slice k
+  for (int h = kCsSlices / 2; h >= 1; h /= 2) {
+    __syncthreads();
+    if (ty < h) {
+      part[0][ty][tx] = part[0][ty][tx] + part[0][ty + h][tx];
+      part[1][ty][tx] = part[1][ty][tx] + part[1][ty + h][tx];
+    }
+  }
   __syncthreads();
   if (ty == 0 && j < p.cols) {
-    double X = (part[0][0][tx] + part[0][1][tx]) + (part[0][2][tx] + part[0][3][tx]);
-    double W = (part[1][0][tx] + part[1][1][tx]) + (part[1][2][tx] + part[1][3][tx]);
-    double rx = sqrt(X / (double)p.rows_x), rw = sqrt(W / (double)p.rows_w);
+    double rx = sqrt(part[0][0][tx] / (double)p.rows_x), rw = sqrt(part[1][0][tx] / (double)p.rows_w);
     double tj = (rx == 0.0 || rw == 0.0) ? 1.0 : pow(rw / rx, p.alpha);
     float tf = (float)tj;
     p.t[j] = tf;
@@ -1168,8 +1181,8 @@ hipError_t launch_dequantize(int fmt, int block, const DequantParams& p, hipStre
 }
 
 hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s) {
-  int grid = (int)((p.cols + 63) / 64);
-  hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  int grid = (int)((p.cols + kCsCols - 1) / kCsCols);
+  hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(kCsThreads), 0, s, p);
   return hipGetLastError();
 }
 
