@@ -931,23 +931,49 @@ __device__ __forceinline__ void block_max_to_global(uint32_t m, unsigned int* ds
   }
 }
 
-template <bool BF16>
+// CONTIG: rows are contiguous (ld == cols) and there is no channel scale, so
+// chunk c starts at element c * L, and two chunks are loaded per iteration
+template <bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void amax_kernel(QuantParams p) {
   constexpr int L = 8;
+  constexpr int U = CONTIG ? 2 : 1;
   const bool chan = p.chan_scale != nullptr;
   const bool had = p.hadamard == 32;
   const int64_t cpr = p.cols / L;
   const int64_t total = p.rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t m = 0;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c - threadIdx.x < total; c += stride) {
-    const bool valid = c < total;
-    const int64_t cc = valid ? c : total - 1;
-    float x[L];
-    load_chunk<L, BF16>(p, cc / cpr, (cc % cpr) * L, x, chan, had);
-    if (valid)
+  // whole waves stay in the loop so that the Hadamard exchanges see their
+  // partners; lanes past the end work on the last chunk and are not counted
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c - threadIdx.x < total; c += U * stride) {
+    if constexpr (CONTIG) {
+      Raw<L, BF16> raw[U];
+      int64_t cu[U];
+      bool vu[U];
 #pragma unroll
-      for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+      for (int u = 0; u < U; ++u) {
+        vu[u] = c + u * stride < total;
+        cu[u] = vu[u] ? c + u * stride : total - 1;
+        load_raw<L, BF16>(p, 0, cu[u] * L, raw[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // both chunks' loads before the first wait
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[L];
+        finish_chunk<L, BF16, false>(p, cu[u] * L, raw[u], x, false, had);
+        if (vu[u])
+#pragma unroll
+          for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+      }
+    } else {
+      const bool valid = c < total;
+      const int64_t cc = valid ? c : total - 1;
+      float x[L];
+      load_chunk<L, BF16>(p, cc / cpr, (cc % cpr) * L, x, chan, had);
+      if (valid)
+#pragma unroll
+        for (int i = 0; i < L; ++i) m = max(m, fbits(x[i]) & 0x7FFFFFFFu);
+    }
   }
   block_max_to_global(m, (unsigned int*)p.global);
 }
@@ -1134,8 +1160,14 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
     hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
     if (p.cols % 8 == 0) {
       int grid = grid_for(p.rows * (p.cols / 8), 256 * 4);
-      if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+      const bool contig = p.ld == p.cols && p.chan_scale == nullptr;
+      if (contig) {
+        if (bf16) hipLaunchKernelGGL((amax_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((amax_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, p);
+      } else {
+        if (bf16) hipLaunchKernelGGL((amax_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((amax_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      }
     } else {
       int grid = grid_for(p.rows * (p.cols / 4), 256 * 4);
       if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);

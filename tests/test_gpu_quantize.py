@@ -237,6 +237,18 @@ def test_auto_global_launch_paths(B, rows, cols):
     run_pair(B, x, xg, "razer_w", 16, "absmax", "auto", special=SPECIAL)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rows,cols", [(61, 512), (2100, 1024)])
+def test_auto_global_contiguous_hadamard(B, bf16, rows, cols):
+    # the separate abs-max pass on contiguous rows with the block-Hadamard
+    # applied (no channel scale); at 2100 x 1024 the second chunk a thread
+    # loads per iteration is live for part of the grid
+    x = datagen.student_t((rows, cols), 970 + rows, 3.0)
+    xn, xg = to_input(x, bf16)
+    run_pair(B, xn, xg, "nvfp4", 16, "absmax", "auto", had=32)
+    run_pair(B, xn, xg, "razer_w", 16, "absmax", "auto", had=32, special=SPECIAL)
+
+
 def test_razer_decode_workload(B):
     w = datagen.razer_decode(1)["W"]
     sampled_parity(B, w, dev(w), "razer_w", 16, "absmax", "auto", sample_rows(17408, 64, 30), special=SPECIAL)
