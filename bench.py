@@ -57,7 +57,7 @@ class Prefill:
     M, K, NS = 32768, 5120, (10240, 17408, 5120)
     compute_dtype = "f16"
     gemm_kernel = "gemm_tile_kernel"
-    quant_kernel = "quantize_kernel"
+    quant_kernel = "nv16_kernel"
 
     def __init__(self, B):
         import torch
@@ -92,15 +92,17 @@ class Prefill:
         self.B.quantize(self.x, "nvfp4", 16, "4over6", "given", global_=self.g_act, codes=self.codes,
                         scales=self.scales)
 
+    def gemm_calls(self, ev=None):
+        for i, (wc, ws, wg, out) in enumerate(self.w):
+            if ev: ev.mark(f"g{i}s")
+            self.B.gemm("nvfp4", self.codes, self.scales, self.g_act, "nvfp4", wc, ws, wg, out=out)
+            if ev: ev.mark(f"g{i}")
+
     def step(self, ev=None):
-        B = self.B
         if ev: ev.mark("q0")
         self.quantize_call()
         if ev: ev.mark("q1")
-        for i, (wc, ws, wg, out) in enumerate(self.w):
-            if ev: ev.mark(f"g{i}s")
-            B.gemm("nvfp4", self.codes, self.scales, self.g_act, "nvfp4", wc, ws, wg, out=out)
-            if ev: ev.mark(f"g{i}")
+        self.gemm_calls(ev)
 
 
 class MxLinear:
@@ -108,7 +110,7 @@ class MxLinear:
     M, K, N = 4096, 4096, 14336
     compute_dtype = "fp4"
     gemm_kernel = "gemm_tile_kernel"
-    quant_kernel = "quantize_kernel"
+    quant_kernel = "mx32_kernel"
 
     def __init__(self, B):
         import torch
@@ -137,14 +139,16 @@ class MxLinear:
         self.B.quantize(self.x, "mxfp4", 32, "absmax", "none", chan_scale=self.t, hadamard=32,
                         codes=self.codes, scales=self.scales)
 
+    def gemm_calls(self, ev=None):
+        if ev: ev.mark("g0s")
+        self.B.gemm("mxfp4", self.codes, self.scales, None, "mxfp4", self.wc, self.ws, None, out=self.out)
+        if ev: ev.mark("g0")
+
     def step(self, ev=None):
-        B = self.B
         if ev: ev.mark("q0")
         self.quantize_call()
         if ev: ev.mark("q1")
-        if ev: ev.mark("g0s")
-        B.gemm("mxfp4", self.codes, self.scales, None, "mxfp4", self.wc, self.ws, None, out=self.out)
-        if ev: ev.mark("g0")
+        self.gemm_calls(ev)
 
 
 class RazerDecode:
@@ -215,14 +219,17 @@ class RazerDecode:
         self.B.quantize(self.x, "razer_a", 16, "absmax", "auto", global_=self.g, codes=self.codes,
                         scales=self.scales)
 
+    def gemm_calls(self, ev=None):
+        if ev: ev.mark("g0s")
+        self.B.gemm("razer_a", self.codes, self.scales, self.g, "razer_w", self.wc, self.ws, self.wg, self.sp,
+                    out=self.out)
+        if ev: ev.mark("g0")
+
     def step(self, ev=None):
-        B = self.B
         if ev: ev.mark("q0")
         self.quantize_call()
         if ev: ev.mark("q1")
-        if ev: ev.mark("g0s")
-        B.gemm("razer_a", self.codes, self.scales, self.g, "razer_w", self.wc, self.ws, self.wg, self.sp, out=self.out)
-        if ev: ev.mark("g0")
+        self.gemm_calls(ev)
 
 
 WORKLOADS = {"prefill": Prefill, "mxfp4_linear": MxLinear, "razer_decode": RazerDecode}
@@ -464,6 +471,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-scaling copy kernel and exit")
     ap.add_argument("--quant-sweep", action="store_true",
                     help="time the NVFP4 quantizer over rules x block sizes on 4096 x 4096 FP32, print one JSON line, exit")
+    ap.add_argument("--only", choices=["quantize", "gemm"],
+                    help="run 20 launches of the workload's quantize (or its GEMMs) and exit: a short program "
+                         "for rocprofv3 counter runs")
     ap.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--traffic-record", nargs=5,
@@ -498,6 +508,15 @@ def main():
         return
 
     wl = WORKLOADS[args.workload](B)
+    if args.only:
+        for i in range(20):
+            if args.only == "quantize":
+                wl.quantize_call()
+            else:
+                wl.gemm_calls()
+        torch.cuda.synchronize()
+        log(f"[bench] 20 {args.only} launches of {wl.config()['workload']} done")
+        return
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         wl.step()

@@ -1,6 +1,6 @@
 """Build libfp4q.so in-tree with hipcc for gfx950.
 
-    python block_scaled_fp4_e4m3_amd/build.py
+    python block_scaled_fp4_e4m3_amd/build.py [--changed]
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel),
 then linked into block_scaled_fp4_e4m3_amd/libfp4q.so.
@@ -44,10 +44,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def _stale(src: str) -> bool:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src), os.path.join(CSRC, "fp4q_internal.hpp"),
+            os.path.join(os.path.dirname(PKG), "include", "fp4q.h")]
+    return any(os.path.getmtime(d) > os.path.getmtime(obj) for d in deps)
+
+
+def build(verbose: bool = True, changed_only: bool = False) -> str:
+    """Compile every source (or, with changed_only, those newer than their
+    objects) and link libfp4q.so."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    todo = [s for s in SOURCES if _stale(s)] if changed_only else SOURCES
+    with ThreadPoolExecutor(max_workers=max(1, min(len(todo), os.cpu_count() or 1))) as ex:
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
@@ -57,4 +70,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(changed_only="--changed" in sys.argv[1:])

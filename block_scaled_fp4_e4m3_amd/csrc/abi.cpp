@@ -158,7 +158,7 @@ fp4q_status fp4q_gemm_w4a4(fp4q_format fa, const uint8_t* a_codes, const uint8_t
   p.c = c;
   p.ldc = ldc;
   p.c_bf16 = c_dtype == FP4Q_BF16;
-  return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream));
+  return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{nullptr, kSplitWorkspaceBytes}));
 }
 
 fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x, int64_t ldx,

@@ -42,8 +42,13 @@ struct GemmParams {
   float w_special[4];
   int64_t M, N, K;
   void* c; int64_t ldc; int c_bf16;
-  int splits;  // K-splits per output tile (1, or > 1 with FP32 atomics into a zeroed C)
+  int splits;       // K-splits per output tile (set by the launcher)
+  float* partials;  // splits > 1: the splits' RN32(g * acc_s), dense M x N slices, added in split order
 };
+
+// bytes of the split-K workspace a matmul may use (per stream, or the
+// library's own array for the non-allocating entry point)
+constexpr size_t kSplitWorkspaceBytes = size_t(32) << 20;
 
 struct ChanScaleParams {
   const void* x; int x_bf16; int64_t rows_x, ldx;
@@ -56,7 +61,17 @@ struct ChanScaleParams {
 hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantParams& p,
                            hipStream_t s);
 hipError_t launch_dequantize(int fmt, int block, const DequantParams& p, hipStream_t s);
-hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s);
+// Device memory for the partial results of K splits: `fixed` if set, else
+// the stream's own workspace, allocated when a launch first splits K (see
+// split_workspace); bytes = 0: no splits.
+struct Workspace {
+  float* fixed;
+  size_t bytes;
+};
+hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s, const Workspace& ws);
+// the split-K workspace of stream s on the current device (allocated on first
+// use, kept until the process ends), or nullptr
+float* split_workspace(hipStream_t s);
 hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s);
 
 // compile-time loop: f(std::integral_constant<int, I>) for I in [B, E); used

@@ -42,6 +42,9 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <algorithm>
+#include <mutex>
+#include <map>
 
 namespace fp4q {
 namespace {
@@ -1140,7 +1143,6 @@ __device__ __forceinline__ void nv_tile_dl(const GemmParams& p, int64_t m0, int6
   if (np > 1) nv_prologue_dl<FA, FW, true>(pbuf(0), pbuf(1), L, kb, ad, sel, R);
   else nv_prologue_dl<FA, FW, false>(pbuf(0), pbuf(1), L, kb, ad, sel, R);
   // the chunk-0 pairs and step-0 decode of stage 0
-  using K0 = std::integral_constant<int, 0>;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     R.pa0[i] = scale_pair_f16<FA, 0>(R.ra[i]);
@@ -1223,7 +1225,7 @@ void gemm_tile_kernel(GemmParams p) {
   const bool inside = row0 + 128 <= p.M && col0 + 128 <= p.N;
   constexpr int ES = OUT_BF16 ? 2 : 4;  // output element bytes
   const int64_t pitch = p.ldc * ES;
-  if (inside && (OUT_BF16 || p.splits == 1) && pitch < (int64_t)1 << 23) {
+  if (inside && p.splits == 1 && pitch < (int64_t)1 << 23) {
     // a whole wave tile and plain stores: a buffer view of the wave tile's
     // first element, the lane's column and row quad in the vector offset, the
     // rest of each element's offset (row within the tile, column block) scalar
@@ -1265,12 +1267,13 @@ void gemm_tile_kernel(GemmParams p) {
         const int64_t row = row0 + 32 * i + (r / 4) * 8 + kh * 4 + (r % 4);
         if (!inside && (row >= p.M || col >= p.N)) continue;
         const float v = gg * acc[i][j][r];
-        if constexpr (OUT_BF16) {
+        if (p.splits > 1) {
+          // this split's RN32(g * acc) into its own dense M x N slice
+          p.partials[(split * p.M + row) * p.N + col] = v;
+        } else if constexpr (OUT_BF16) {
           uint32_t u = __float_as_uint(v);
           u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
           ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
-        } else if (p.splits > 1) {
-          atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
         } else {
           ((float*)p.c)[row * p.ldc + col] = v;
         }
@@ -1279,17 +1282,36 @@ void gemm_tile_kernel(GemmParams p) {
   }
 }
 
-// FP32 C rows [0, M) x columns [0, N) <- 0 (ahead of split-K accumulation);
-// rows are 16-byte aligned (pitch and base), four columns per thread
-__global__ __launch_bounds__(256) void zero_c_kernel(float* c, int64_t M, int64_t N, int64_t ldc) {
-  const int64_t col = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (col >= N) return;
-  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
-    float* dst = c + row * ldc + col;
-    if (col + 4 <= N) *(float4*)dst = make_float4(0.f, 0.f, 0.f, 0.f);
-    else
-      for (int64_t j = 0; j < N - col; ++j) dst[j] = 0.0f;
+// C = the splits' partial results added in split order, RN32 at each step:
+// ((p_0 + p_1) + p_2) + ...; stored fp32, or bf16 rounded to nearest even from
+// that FP32 sum.  partials: splits dense M x N slices.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                                             int64_t N, void* c, int64_t ldc) {
+  const int64_t total = M * N, slice = M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int sp = 1; sp < splits; ++sp) v = v + part[sp * slice + i];
+    const int64_t row = i / N, col = i - row * N;
+    if constexpr (OUT_BF16) {
+      uint32_t u = __float_as_uint(v);
+      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      ((uint16_t*)c)[row * ldc + col] = (uint16_t)u;
+    } else {
+      ((float*)c)[row * ldc + col] = v;
+    }
   }
+}
+
+hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
+  const int64_t blocks = std::min<int64_t>((p.M * p.N + 255) / 256, 256 * 8);
+  if (p.c_bf16)
+    hipLaunchKernelGGL(reduce_splits_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, p.partials, p.splits, p.M,
+                       p.N, p.c, p.ldc);
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, p.partials, p.splits,
+                       p.M, p.N, p.c, p.ldc);
+  return hipGetLastError();
 }
 
 // per-device caches of launch facts (0: not yet known); every thread that
@@ -1314,16 +1336,22 @@ int device_cus() {
   return cus;
 }
 
-// K-splits for an FP32 output with too few tiles to fill the chip: the count
-// that minimises (rounds of workgroups over the CUs) x (stages per split),
-// at most 4 (each split adds one read-modify-write of C)
-int choose_splits(const GemmParams& p, int64_t T) {
+float* ws_pointer(const Workspace& ws, hipStream_t s) { return ws.fixed ? ws.fixed : split_workspace(s); }
+
+// K-splits for a launch with too few tiles to fill the chip: the count that
+// minimises (rounds of workgroups over the CUs) x (stages per split), at most
+// 4, and only as many as the workspace holds partial results for.  Each split
+// writes RN32(g * acc_s) of its stage range to its own slice of the
+// workspace; reduce_splits_kernel adds the slices in split order, so the
+// result does not depend on which split finishes first.
+int choose_splits(const GemmParams& p, int64_t T, size_t ws_bytes) {
   const int cus = device_cus();
-  if (p.c_bf16 || T >= cus) return 1;
+  if (T >= cus || ws_bytes == 0) return 1;
   const int64_t nst = (p.K + BK - 1) / BK;
+  const int64_t fit = (int64_t)(ws_bytes / ((size_t)p.M * (size_t)p.N * sizeof(float)));
   int best = 1;
   int64_t best_cost = ((T + cus - 1) / cus) * nst;
-  for (int sp = 2; sp <= 4 && sp <= nst; ++sp) {
+  for (int sp = 2; sp <= 4 && sp <= nst && sp <= fit; ++sp) {
     const int64_t cost = ((T * sp + cus - 1) / cus) * ((nst + sp - 1) / sp);
     if (cost < best_cost) { best = sp; best_cost = cost; }
   }
@@ -1331,18 +1359,30 @@ int choose_splits(const GemmParams& p, int64_t T) {
 }
 
 template <int FA, int FW>
-hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
+hipError_t launch_tile(const GemmParams& p0, hipStream_t s, const Workspace& ws) {
   const int64_t T = ((p0.M + BM - 1) / BM) * ((p0.N + BN - 1) / BN);
   GemmParams p = p0;
-  p.splits = choose_splits(p0, T);
-  if (p.splits > 1) {
-    const unsigned gx = (unsigned)((p.N + 1023) / 1024), gy = (unsigned)(p.M < 1024 ? p.M : 1024);
-    hipLaunchKernelGGL(zero_c_kernel, dim3(gx, gy), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
+  int sp = choose_splits(p0, T, ws.bytes);
+  if (sp > 1 && (p.partials = ws_pointer(ws, s)) == nullptr) sp = 1;
+  if (sp > 1) {
+    // the kernel's stage ranges (whole groups of stages on the LDS-DMA paths):
+    // launch only splits that own stages, so that every slice is written
+    constexpr int DLG = FA == MXFP4 ? kDlGroup : 2;
+    const bool dl = p.K % (DLG * BK) == 0 &&
+                    ((((uintptr_t)p.a_codes | (uintptr_t)p.w_codes | (uintptr_t)p.a_scales | (uintptr_t)p.w_scales) &
+                      15) == 0);
+    const int64_t nst = (p.K + BK - 1) / BK;
+    int64_t per = (nst + sp - 1) / sp;
+    if (dl) per = (per + DLG - 1) / DLG * DLG;
+    sp = (int)((nst + per - 1) / per);
   }
+  p.splits = sp;
   const unsigned grid = (unsigned)(T * p.splits);
   if (p.c_bf16) hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, true>), dim3(grid), dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL((gemm_tile_kernel<FA, FW, false>), dim3(grid), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.splits > 1) e = launch_reduce(p, s);
+  return e;
 }
 
 // ---------------------------------------------------------------- small M
@@ -1359,8 +1399,9 @@ hipError_t launch_tile(const GemmParams& p0, hipStream_t s) {
 // MFMAs; one 16-byte load per lane brings a turn's scales (4 blocks of each
 // of 4 chunks of its row), and a window's first turn also loads the wave's
 // share of the next window's A.  The decode and the K
-// permutation are those of the tile kernel.  The splits of K, whole windows
-// each, add into a zero-filled FP32 C with atomics.
+// permutation are those of the tile kernel.  K may be split in ranges of
+// whole windows; each split writes its partial results to the workspace and
+// reduce_splits_kernel adds them in split order (see choose_splits).
 //
 // No load is conditional: windows are full, the last window is peeled and its
 // last turn issues no refills.  Loads complete in issue order, and with the
@@ -1559,12 +1600,12 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
       const int64_t row = 32 * b + (r / 4) * 8 + kh * 4 + (r % 4);
       if (row >= p.M) continue;
       const float v = gg * acc[b][r];
-      if constexpr (OUT_BF16) {
+      if (p.splits > 1) {
+        p.partials[(split * p.M + row) * p.N + col] = v;
+      } else if constexpr (OUT_BF16) {
         uint32_t u = __float_as_uint(v);
         u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
         ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)u;
-      } else if (p.splits > 1) {
-        atomicAdd(&((float*)p.c)[row * p.ldc + col], v);
       } else {
         ((float*)p.c)[row * p.ldc + col] = v;
       }
@@ -1582,30 +1623,31 @@ bool small_m_fits(const GemmParams& p) {
   return p.M <= kSmallM && p.K % (64 * sm_win(sm_blocks(p.M))) == 0 && (a & 15u) == 0;
 }
 
-// FP32 output splits K: the split count minimises an estimate of the time,
-// rounds of resident workgroups x chunks per split plus the FP32 atomics the
-// splits add (measured on MI355X: about 1.1 us per chunk and round, 3.2 us
-// per million atomics)
-int64_t sm_choose_splits(int64_t M, int64_t N, int64_t nch, int64_t slabs, int64_t slots, int win) {
+// The split count minimises an estimate of the time: rounds of resident
+// workgroups x chunks per split, plus the partial results the splits write
+// and the reduction reads and its launch (measured on MI355X: about 1.1 us
+// per chunk and round; about 3.2 us per million partial results and 2 us for
+// the reduction launch), among the counts whose partials fit the workspace
+int64_t sm_choose_splits(int64_t M, int64_t N, int64_t nch, int64_t slabs, int64_t slots, int win, int64_t fit) {
   int64_t best = 1;
   double best_t = 1e300;
-  for (int64_t sp = 1; sp <= nch / win; ++sp) {
+  for (int64_t sp = 1; sp <= nch / win && sp <= std::max<int64_t>(fit, 1); ++sp) {
     const int64_t len = sm_split_len(nch, sp, win), used = (nch + len - 1) / len;
     if (used != sp) continue;
     const double rounds = (double)((slabs * sp + slots - 1) / slots);
-    const double t = rounds * (double)len * 1.1 + (sp > 1 ? 3.2e-6 * (double)(sp * M * N) : 0.0);
+    const double t = rounds * (double)len * 1.1 + (sp > 1 ? 3.2e-6 * (double)(sp * M * N) + 2.0 : 0.0);
     if (t < best_t) { best_t = t; best = sp; }
   }
   return best;
 }
 
 template <int FA, int FW, int MR>
-hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s) {
+hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspace& ws) {
   constexpr int WIN = SmCfg<MR>::WIN, WAVES = SmCfg<MR>::WAVES;
   GemmParams p = p0;
   const int64_t slabs = (p.N + 32 * WAVES - 1) / (32 * WAVES), nch = p.K / 64;
   int64_t sp = 1;
-  if (!p.c_bf16) {
+  if (ws.bytes > 0) {
     // resident workgroups per CU, as the runtime reports them for this kernel
     static std::atomic<int> cache[kMaxDevices];
     const int dev = current_device();
@@ -1618,51 +1660,74 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s) {
       per_cu = nb;
       if (dev >= 0) cache[dev].store(per_cu, std::memory_order_relaxed);
     }
-    sp = sm_choose_splits(p.M, p.N, nch, slabs, (int64_t)per_cu * device_cus(), WIN);
+    const int64_t fit = (int64_t)(ws.bytes / ((size_t)p.M * (size_t)p.N * sizeof(float)));
+    sp = sm_choose_splits(p.M, p.N, nch, slabs, (int64_t)per_cu * device_cus(), WIN, fit);
+    if (sp > 1 && (p.partials = ws_pointer(ws, s)) == nullptr) sp = 1;
   }
   p.splits = (int)sp;
-  if (sp > 1) {
-    const unsigned gx = (unsigned)((p.N + 1023) / 1024), gy = (unsigned)(p.M < 1024 ? p.M : 1024);
-    hipLaunchKernelGGL(zero_c_kernel, dim3(gx, gy), dim3(256), 0, s, (float*)p.c, p.M, p.N, p.ldc);
-  }
   const unsigned grid = (unsigned)(slabs * sp);
   const unsigned threads = 64 * WAVES;
   if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR>), dim3(grid), dim3(threads), 0, s, p);
   else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR>), dim3(grid), dim3(threads), 0, s, p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.splits > 1) e = launch_reduce(p, s);
+  return e;
 }
 
 template <int FA, int FW>
-hipError_t launch_small_m(const GemmParams& p, hipStream_t s) {
+hipError_t launch_small_m(const GemmParams& p, hipStream_t s, const Workspace& ws) {
   switch (sm_blocks(p.M)) {
-    case 1: return launch_small_m_mr<FA, FW, 1>(p, s);
-    case 2: return launch_small_m_mr<FA, FW, 2>(p, s);
-    default: return launch_small_m_mr<FA, FW, 4>(p, s);
+    case 1: return launch_small_m_mr<FA, FW, 1>(p, s, ws);
+    case 2: return launch_small_m_mr<FA, FW, 2>(p, s, ws);
+    default: return launch_small_m_mr<FA, FW, 4>(p, s, ws);
   }
 }
 
 template <int FA, int FW>
-hipError_t launch_nv(const GemmParams& p, hipStream_t s) {
-  if (small_m_fits(p)) return launch_small_m<FA, FW>(p, s);
-  return launch_tile<FA, FW>(p, s);
+hipError_t launch_nv(const GemmParams& p, hipStream_t s, const Workspace& ws) {
+  if (small_m_fits(p)) return launch_small_m<FA, FW>(p, s, ws);
+  return launch_tile<FA, FW>(p, s, ws);
 }
 
 template <int FA>
-hipError_t launch_nv_a(int fw, const GemmParams& p, hipStream_t s) {
+hipError_t launch_nv_a(int fw, const GemmParams& p, hipStream_t s, const Workspace& ws) {
   switch (fw) {
-    case RAZER_A: return launch_nv<FA, RAZER_A>(p, s);
-    case RAZER_W: return launch_nv<FA, RAZER_W>(p, s);
-    default: return launch_nv<FA, NVFP4>(p, s);
+    case RAZER_A: return launch_nv<FA, RAZER_A>(p, s, ws);
+    case RAZER_W: return launch_nv<FA, RAZER_W>(p, s, ws);
+    default: return launch_nv<FA, NVFP4>(p, s, ws);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s) {
-  if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (fa == MXFP4) return launch_tile<MXFP4, MXFP4>(p, s);
-  if (fa == RAZER_A) return launch_nv_a<RAZER_A>(fw, p, s);
-  return launch_nv_a<NVFP4>(fw, p, s);
+// Split-K workspace of one stream: allocated on the stream's first matmul
+// and kept until the process ends.  Work on one stream runs in order, so the
+// launches of one stream can share it; different streams (and devices) get
+// their own.  nullptr if the allocation failed: that stream runs unsplit.
+float* split_workspace(hipStream_t s) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, void*> cache;
+  const std::pair<int, hipStream_t> key(current_device(), s);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return (float*)it->second;
+  void* ptr = nullptr;
+  if (hipMalloc(&ptr, kSplitWorkspaceBytes) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error: the launches below must not report it
+    ptr = nullptr;
+  }
+  cache[key] = ptr;
+  return (float*)ptr;
+}
+
+hipError_t launch_gemm(int fa, int fw, const GemmParams& p0, hipStream_t s, const Workspace& ws) {
+  if (p0.M == 0 || p0.N == 0) return hipSuccess;
+  GemmParams p = p0;
+  p.partials = nullptr;
+  p.splits = 1;
+  if (fa == MXFP4) return launch_tile<MXFP4, MXFP4>(p, s, ws);
+  if (fa == RAZER_A) return launch_nv_a<RAZER_A>(fw, p, s, ws);
+  return launch_nv_a<NVFP4>(fw, p, s, ws);
 }
 
 }  // namespace fp4q

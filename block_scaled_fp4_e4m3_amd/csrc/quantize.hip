@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace fp4q {
 
 namespace {
@@ -87,7 +89,6 @@ template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
 template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0; };
 template <> struct FmtTraits<RAZER_W> { static constexpr int SF = 1, KMAX = 63,  NSP = 4; };
-template <> struct FmtTraits<MXFP4>   { static constexpr int SF = 2; };
 
 // LDS tables, built once per workgroup for the launch's global scale g
 template <int FMT>
@@ -101,7 +102,7 @@ struct Tables {
   uint32_t sp_hi[KN][NSP];    // special interval, strict <
   float spv[NSP];             // special values
 };
-template <> struct Tables<MXFP4> { uint32_t dummy; };
+template <> struct Tables<MXFP4> { uint32_t dummy; };  // kernels without tables
 
 // Nearest standard E2M1 magnitudes below/above |v| (|v| in (2, 7.5], not on the grid)
 __device__ __forceinline__ void special_bounds(float av, float& lo, float& hi, bool& open_hi) {
@@ -256,9 +257,12 @@ template <int L, bool BF16>
 __device__ __forceinline__ void load_raw(const QuantParams& p, int64_t r, int64_t j0, Raw<L, BF16>& raw) {
   if constexpr (BF16) {
     const uint16_t* src = (const uint16_t*)p.x + r * p.ld + j0;
-    if constexpr (L == 8) {
-      const uint4 v = *(const uint4*)src;
-      raw.w[0] = v.x; raw.w[1] = v.y; raw.w[2] = v.z; raw.w[3] = v.w;
+    if constexpr (L >= 8) {
+#pragma unroll
+      for (int i = 0; i < L / 2; i += 4) {
+        const uint4 v = *(const uint4*)(src + 2 * i);
+        raw.w[i] = v.x; raw.w[i + 1] = v.y; raw.w[i + 2] = v.z; raw.w[i + 3] = v.w;
+      }
     } else {
       const uint2 v = *(const uint2*)src;
       raw.w[0] = v.x; raw.w[1] = v.y;
@@ -397,27 +401,6 @@ __device__ __forceinline__ uint32_t clear_neg_zero(uint32_t packed) {
   return packed & ~(packed & 0x88888888u & ~nz);
 }
 
-// Bracketed hardware encode.  The gfx950 FP4 convert rounds to nearest even
-// (saturating) after dividing by the power-of-two part of its scale, which is
-// 1 here.  Each element is converted at x * rlo and x * rhi, where
-// rlo < 1/(s g) < rhi with a relative margin far above the rounding errors of
-// forming them and of the product, so the exact ratio |x| / (s g) lies
-// strictly between the two converted values.  Rounding is monotone: equal
-// codes at both ends are the exact decision.  `ok` is false when some element
-// may sit on or near a rounding midpoint; that block then takes the threshold
-// path.
-template <int L>
-__device__ __forceinline__ uint32_t encode_bracket(const float* x, float rlo, float rhi, bool& ok) {
-  uint32_t plo = 0, phi = 0;
-  static_for<0, L / 2>([&](auto ic) {
-    constexpr int b = decltype(ic)::value;
-    plo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(plo, x[2 * b] * rlo, x[2 * b + 1] * rlo, 1.0f, b);
-    phi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(phi, x[2 * b] * rhi, x[2 * b + 1] * rhi, 1.0f, b);
-  });
-  ok = plo == phi;
-  return clear_neg_zero(plo);
-}
-
 template <int LPB>
 __device__ __forceinline__ bool group_all(bool v) {
   uint32_t b = v ? 1u : 0u;
@@ -471,32 +454,6 @@ __device__ __forceinline__ bool past_midpoint(float ax, float Q, float g, bool o
   return r1 > plo || (r1 == plo && odd);
 }
 
-// Exact codes from low-side codes.  `plo` holds the codes of x * rlo with
-// rlo < 1/(s g): every element's exact code is its low-side code or one
-// magnitude step above (the exact ratio exceeds the low-side ratio by far less
-// than the gap between midpoints).  Step up where |x| is past the midpoint
-// above the low-side magnitude; magnitude 7 (6.0) is the top.
-template <int L>
-__device__ __forceinline__ uint32_t resolve_codes(const float* x, uint32_t plo, float s, float g) {
-  const uint32_t inc = (plo & 0x77777777u) + 0x11111111u;  // magnitude + 1 per nibble
-  uint32_t up = 0;
-  static_for<0, L / 2>([&](auto ic) {
-    constexpr int b = decltype(ic)::value;
-    // half values of the low-side and next magnitudes: their sum is the midpoint
-    const auto vl = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(plo, 0.5f, b);
-    const auto vu = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(inc, 0.5f, b);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * b + h;
-      const uint32_t mag = (plo >> (4 * i)) & 7u;
-      const float mid = fabsf(vl[h]) + vu[h];
-      const bool go = mag != 7u && past_midpoint(fabsf(x[i]), mid * s, g, (mag & 1u) != 0);
-      up |= go ? (0xFu << (4 * i)) : 0u;
-    }
-  });
-  return (plo & ~up) | (((inc & 0x77777777u) | (plo & 0x88888888u)) & up);
-}
-
 // MXFP4 codes by the exact threshold search (a wave with a non-finite block,
 // or a shared exponent below the normal range): thresholds 2^E times the E2M1
 // midpoints (exact), as bit patterns, strict > for the even ones and >= (one
@@ -533,12 +490,45 @@ __device__ __attribute__((noinline)) uint32_t encode_nv_thresholds(float __attri
   return plo;
 }
 
+// Elements whose codes at x * rlo and x * rhi differ sit on or near a
+// rounding midpoint.  Each one's exact code is its low-side code or one
+// magnitude step above (the bracket is far narrower than the gap between
+// midpoints); the exact midpoint test decides.  One element per lane per pass,
+// in a wave-uniform loop that almost always runs once.  Out of line, with the
+// elements by value: inlined, the selection of the element by its index makes
+// the compiler keep the caller's element array in LDS.
+template <int L>
+__device__ __attribute__((noinline)) uint32_t resolve_ambiguous(float __attribute__((ext_vector_type(L))) x,
+                                                                uint32_t plo, uint32_t phi, float s, float g) {
+  uint32_t amb = plo ^ phi;
+  while (!wave_all(amb == 0)) {
+    const int sh = amb ? (int)(__builtin_ctz(amb) & ~3) : 0;  // 4 * element index
+    float xi = x[0];
+#pragma unroll
+    for (int j = 1; j < L; ++j) xi = (sh == 4 * j) ? x[j] : xi;
+    const uint32_t mag = (plo >> sh) & 7u;
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(mag | ((mag + 1u) << 4), 0.5f, 0);
+    const bool go = amb != 0 && mag != 7u && past_midpoint(fabsf(xi), (v[0] + v[1]) * s, g, (mag & 1u) != 0);
+    plo += go ? (1u << sh) : 0u;  // magnitude + 1 (at most 7: no carry)
+    amb &= ~(0xFu << sh);
+  }
+  return plo;
+}
+
+// Bracketed hardware encode.  The gfx950 FP4 convert rounds to nearest even
+// (saturating) after dividing by the power-of-two part of its scale, which is
+// 1 here.  Each element is converted at x * rlo and x * rhi, where
+// rlo < 1/(s g) < rhi with a relative margin far above the rounding errors of
+// forming them and of the product, so the exact ratio |x| / (s g) lies
+// strictly between the two converted values.  Rounding is monotone: equal
+// codes at both ends are the exact decision.
+//
 // NVFP4 codes of a lane's L elements for scale code k (value s) under global
-// g: bracketed convert; when some element of the wave cannot be decided that
-// way (on or near a midpoint), the whole wave resolves its elements exactly
-// from the low-side codes.  The bracket is used only for finite blocks with
-// s g well inside the normal range; a wave with any other block takes the
-// threshold search.
+// g: the bracketed convert; when some element of the wave cannot be decided
+// that way, the whole wave resolves its ambiguous elements exactly.  The
+// bracket is used only for finite blocks with s g well inside the normal
+// range; a wave with any other block takes the threshold search.
 template <int L, int LPB>
 __device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, float g, bool finite) {
   const float sg = s * g;
@@ -552,28 +542,12 @@ __device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, fl
     phi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(phi, x[2 * b] * rhi, x[2 * b + 1] * rhi, 1.0f, b);
   });
   if (!wave_all(ok && plo == phi)) {
-    if (wave_all(ok)) {
-      // elements whose two ends differ, one per lane per pass (usually one pass)
-      uint32_t amb = plo ^ phi;
-      while (!wave_all(amb == 0)) {
-        const int sh = amb ? (int)(__builtin_ctz(amb) & ~3) : 0;  // 4 * element index
-        float xi = x[0];
+    typedef float fLv __attribute__((ext_vector_type(L)));
+    fLv xv;
 #pragma unroll
-        for (int j = 1; j < L; ++j) xi = (sh == 4 * j) ? x[j] : xi;
-        const uint32_t mag = (plo >> sh) & 7u;
-        typedef float f2v __attribute__((ext_vector_type(2)));
-        const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(mag | ((mag + 1u) << 4), 0.5f, 0);
-        const bool go = amb != 0 && mag != 7u && past_midpoint(fabsf(xi), (v[0] + v[1]) * s, g, (mag & 1u) != 0);
-        plo += go ? (1u << sh) : 0u;  // magnitude + 1 (at most 7: no carry)
-        amb &= ~(0xFu << sh);
-      }
-    } else {
-      typedef float fLv __attribute__((ext_vector_type(L)));
-      fLv xv;
-#pragma unroll
-      for (int i = 0; i < L; ++i) xv[i] = x[i];
-      return encode_nv_thresholds<L>(xv, k, g);
-    }
+    for (int i = 0; i < L; ++i) xv[i] = x[i];
+    if (wave_all(ok)) plo = resolve_ambiguous<L>(xv, plo, phi, s, g);
+    else return encode_nv_thresholds<L>(xv, k, g);
   }
   return clear_neg_zero(plo);
 }
@@ -716,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   // chunk c = r * cpr + cj; the division happens once, then (r, cj) advance.
   // Each iteration issues the loads of U chunks (c, c + stride, ...) before
   // working on the first, to keep enough bytes in flight per CU.
-  constexpr int U = (FMT == MXFP4 && CONTIG) ? 1 : 2;
+  constexpr int U = 2;
   const __amdgpu_buffer_rsrc_t tv = chan_view(p);
   int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   int64_t r0 = CONTIG ? 0 : c / cpr, cj0 = CONTIG ? c : c % cpr;
@@ -761,34 +735,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
     uint32_t packed;
     uint8_t sbyte;
-    if constexpr (FMT == MXFP4) {
-      // MACaQ section 1: shared exponent E = floor(log2 amax) - 2, clamped
-      int E;
-      if (amax == 0) E = -127;
-      else {
-        int ex = (int)(amax >> 23);
-        int fl = ex ? ex - 127 : (31 - __clz((int)amax)) - 149;
-        E = max(-127, fl - 2);
-      }
-      // the convert divides by 2^E exactly (E >= -126: a normal FP32 scale)
-      // and rounds to nearest even, which is the format's rounding
-      if (wave_all(E >= -126 && amax < 0x7F800000u)) {
-        packed = 0;
-        const float sc = bitsf((uint32_t)(E + 127) << 23);
-        static_for<0, L / 2>([&](auto ic) {
-          constexpr int b = decltype(ic)::value;
-          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, x[2 * b], x[2 * b + 1], sc, b);
-        });
-        packed = clear_neg_zero(packed);
-      } else {
-        typedef float fLv __attribute__((ext_vector_type(L)));
-        fLv xv;
-#pragma unroll
-        for (int i = 0; i < L; ++i) xv[i] = x[i];
-        packed = encode_mx_thresholds<L>(xv, E);
-      }
-      sbyte = (uint8_t)(E + 127);
-    } else if constexpr (FMT == NVFP4) {
+    if constexpr (FMT == NVFP4) {
       if constexpr (RULE == BRUTE) {
         // every positive E4M3 scale; strict minimum, ties keep the smaller code
         float best = 0.f;
@@ -876,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       }
       sbyte = (uint8_t)((bestp << 7) | k);
     } else {
-      // RaZeR: abs-max scale (E4M3 for activations, E3M3 for weights), then
-      // the special value with the lowest block error (ties keep the first)
+      // RaZeR-W: the abs-max E3M3 scale, then the special value of the table
+      // with the lowest block error (ties keep the first)
       int k = select_scale<SF>(bitsf(amax), T.smid6, inv6);
       if (p.prevent_zero && k == 0) k = 1;
       uint32_t t[7];
@@ -899,8 +846,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
           if (q == 0 || e < best) { best = e; bestp = q; packed = pk; }
         }
       }
-      if (FMT == RAZER_A) sbyte = (uint8_t)((bestp << 7) | k);
-      else sbyte = (uint8_t)((bestp << 6) | k);
+      sbyte = (uint8_t)((bestp << 6) | k);
     }
 
     if (valid) {
@@ -911,6 +857,265 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     }
     }  // u
   }
+}
+
+// ---------------------------------------------------------------- NVFP4, 16 elements per lane
+// Abs-max and 4-over-6 with blocks of 16 or 32 on contiguous rows without a
+// channel scale (the layout of every activation and weight workload here).
+// The tensor is walked as one row of 16-element runs; lane l of a wave owns
+// run (wave base + l).  A block of 16 is one lane and a block of 32 two
+// adjacent lanes, so the per-block work (abs-max, both scale decisions, the
+// reciprocals) is paid once per 16 elements and the error sums of 16-blocks
+// need no lane exchange.  The run splits into two 8-element words for the
+// FP4 converts; the decisions and the error tree are those of the 8-element
+// kernel: tree(16) = tree(first 8) + tree(last 8).
+
+// codes of 16 elements as two words (elements 0-7, 8-15), -0 not yet cleared
+template <int LPB>
+__device__ __forceinline__ uint2 encode_nv16(const float* x, int k, float s, float g, bool finite) {
+  const float sg = s * g;
+  const float r = __builtin_amdgcn_rcpf(sg);  // within 1 ulp of 1 / RN(s g)
+  const bool ok = finite && sg > 0x1p-120f && sg < 0x1p120f;
+  const float rlo = r * (1.0f - 0x1p-20f), rhi = r * (1.0f + 0x1p-20f);
+  uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
+  static_for<0, 4>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    l0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l0, x[2 * b] * rlo, x[2 * b + 1] * rlo, 1.0f, b);
+    h0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h0, x[2 * b] * rhi, x[2 * b + 1] * rhi, 1.0f, b);
+    l1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l1, x[8 + 2 * b] * rlo, x[9 + 2 * b] * rlo, 1.0f, b);
+    h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h1, x[8 + 2 * b] * rhi, x[9 + 2 * b] * rhi, 1.0f, b);
+  });
+  if (!wave_all(ok && l0 == h0 && l1 == h1)) {
+    typedef float f8v __attribute__((ext_vector_type(8)));
+    f8v xa, xb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { xa[i] = x[i]; xb[i] = x[8 + i]; }
+    if (wave_all(ok)) {
+      l0 = resolve_ambiguous<8>(xa, l0, h0, s, g);
+      l1 = resolve_ambiguous<8>(xb, l1, h1, s, g);
+    } else {
+      l0 = encode_nv_thresholds<8>(xa, k, g);
+      l1 = encode_nv_thresholds<8>(xb, k, g);
+    }
+  }
+  return make_uint2(l0, l1);
+}
+
+// block error of a lane's 16 elements: the balanced tree of the two halves
+__device__ __forceinline__ float lane_sse16(const float* x, uint2 c, float s, float g) {
+  return lane_sse<8>(x, c.x, s, g, false, 0.f) + lane_sse<8>(x + 8, c.y, s, g, false, 0.f);
+}
+
+template <int B, int RULE, bool BF16>
+__global__ __launch_bounds__(kThreads) void nv16_kernel(QuantParams p) {
+  constexpr int L = 16, LPB = B / L;
+  static_assert(LPB == 1 || LPB == 2, "blocks of 16 or 32");
+  const float g = p.global ? *p.global : 1.0f;
+  const bool had = p.hadamard == 32;
+  const int64_t total = p.rows * (p.cols / L);  // runs
+  const double inv6 = 1.0 / (6.0 * (double)g);
+  const double inv4 = 1.0 / (4.0 * (double)g);
+  // scale selection as in quantize_kernel: the hardware FP32 -> E4M3 convert of
+  // amax / (T g) bracketed from below, one exact midpoint test
+  const bool fast_scale = g > 0x1p-100f && g < 0x1p100f;
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * g), r4 = __builtin_amdgcn_rcpf(4.0f * g);
+  const float lo6 = r6 * (1.0f - 0x1p-20f), lo4 = r4 * (1.0f - 0x1p-20f);
+
+  constexpr int U = 2;  // runs whose loads are issued before the first is worked on
+  const int lane = threadIdx.x & 63;
+  const int64_t pass = (int64_t)gridDim.x * kThreads;
+  // wave-uniform base run; whole waves stay in the loop (Hadamard exchanges)
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); c0 < total; c0 += U * pass) {
+    Raw<L, BF16> raw[U];
+    int64_t cu[U];
+    bool vu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * pass + lane;
+      vu[u] = c < total;
+      cu[u] = vu[u] ? c : total - 1;
+      if (c0 + u * pass < total) load_raw<L, BF16>(p, 0, cu[u] * L, raw[u]);  // uniform: the wave has work
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all of the iteration's loads before the first wait
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * pass >= total) break;  // uniform: no run of the wave is left
+      float x[L];
+      finish_chunk<L, BF16, false>(p, cu[u] * L, raw[u], x, false, had);
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+      amax = group_max<LPB>(amax);
+      const bool finite = amax < 0x7F800000u;
+      int k6 = 0, k4 = 0;
+      if (wave_all(fast_scale && finite)) {
+        typedef short s2v __attribute__((ext_vector_type(2)));
+        const float a = bitsf(amax);
+        const s2v z = {0, 0};
+        const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * lo6, a * lo4, 1.0f, false);
+        const uint32_t wl = (uint16_t)clo[0];
+        k6 = e4m3_from_low(wl & 0xFFu, a, 6.0f, g);
+        if constexpr (RULE == FOUR6) k4 = e4m3_from_low(wl >> 8, a, 4.0f, g);
+      } else {
+        k6 = select_e4m3_exact(bitsf(amax), inv6, 6.0 * (double)g);
+        if constexpr (RULE == FOUR6) k4 = select_e4m3_exact(bitsf(amax), inv4, 4.0 * (double)g);
+      }
+      if (p.prevent_zero && k6 == 0) k6 = 1;
+      const float s6 = e4m3_f32(k6);
+      uint2 packed = encode_nv16<LPB>(x, k6, s6, g, finite);
+      int sbyte = k6;
+      if constexpr (RULE == FOUR6) {
+        if (p.prevent_zero && k4 == 0) k4 = 1;
+        const float s4 = e4m3_f32(k4);
+        const uint2 pk4 = encode_nv16<LPB>(x, k4, s4, g, finite);
+        // a -0 code (0x8) decodes to -0 and gives the same error as +0
+        const float e6 = group_sum<LPB>(lane_sse16(x, packed, s6, g));
+        const float e4 = group_sum<LPB>(lane_sse16(x, pk4, s4, g));
+        if (e4 < e6) { packed = pk4; sbyte = k4; }
+      }
+      packed.x = clear_neg_zero(packed.x);
+      packed.y = clear_neg_zero(packed.y);
+      if (vu[u]) {
+        *(uint2*)(p.codes + cu[u] * (L / 2)) = packed;
+        if (LPB == 1 || (lane & 1) == 0) p.scales[cu[u] / LPB] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MXFP4, 32 elements per lane
+// One lane owns a 32-element run: one MXFP4 block and one Hadamard group, so
+// the rotation runs in registers and the block maximum needs no exchange.
+// A thread keeps its run position within the row and walks rows: the grid's
+// thread count is a multiple of the runs per row (the launcher sizes it so),
+// so thread t owns run t mod rpr of rows t / rpr, t / rpr + rstep, ... and
+// loads the run's 32 channel scales once.
+template <bool BF16>
+__device__ __forceinline__ void load_run32(const QuantParams& p, int64_t r, int64_t j0, uint32_t (&w)[BF16 ? 16 : 32]) {
+  constexpr int W = BF16 ? 16 : 32;
+  const uint8_t* src = (const uint8_t*)p.x + (r * p.ld + j0) * (BF16 ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < W; i += 4) {
+    const uint4 v = *(const uint4*)(src + 4 * i);
+    w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+  }
+}
+
+template <bool BF16, bool CHAN, bool HAD>
+__global__ __launch_bounds__(kThreads) void mx32_kernel(QuantParams p) {
+  constexpr int L = 32, W = BF16 ? 16 : 32;
+  const int64_t rpr = p.cols / L;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t rstep = (int64_t)gridDim.x * kThreads / rpr;
+  const int64_t cj = t % rpr, j0 = cj * L;
+  float tc[L];
+  if constexpr (CHAN) {
+#pragma unroll
+    for (int i = 0; i < L; i += 4) {
+      const float4 v = *(const float4*)(p.chan_scale + j0 + i);
+      tc[i] = v.x; tc[i + 1] = v.y; tc[i + 2] = v.z; tc[i + 3] = v.w;
+    }
+  }
+  constexpr int U = 2;  // rows whose loads are issued before the first is worked on
+  for (int64_t r0 = t / rpr; r0 < p.rows; r0 += U * rstep) {
+    // no lane exchange in this kernel, so a lane past the last row simply
+    // loads nothing
+    uint32_t raw[U][W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (r0 + u * rstep < p.rows) load_run32<BF16>(p, r0 + u * rstep, j0, raw[u]);
+      else
+#pragma unroll
+        for (int i = 0; i < W; ++i) raw[u][i] = 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + u * rstep;
+      float x[L];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+          x[2 * i] = bitsf(raw[u][i] << 16);
+          x[2 * i + 1] = bitsf(raw[u][i] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < L; ++i) x[i] = bitsf(raw[u][i]);
+      }
+      if constexpr (CHAN) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) x[i] = x[i] * tc[i];
+      }
+      if constexpr (HAD) {
+        // natural-order FWHT of the 32 values, then the orthonormal factor
+#pragma unroll
+        for (int h = 1; h < L; h *= 2) {
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            if ((i & h) == 0) {
+              const float a = x[i], b = x[i + h];
+              x[i] = a + b;
+              x[i + h] = a - b;
+            }
+          }
+        }
+        const float c = bitsf(0x3E3504F3u);  // RN32(2^-2.5)
+#pragma unroll
+        for (int i = 0; i < L; ++i) x[i] = x[i] * c;
+      }
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+      // MACaQ section 1: shared exponent E = floor(log2 amax) - 2, clamped
+      int E;
+      if (amax == 0) E = -127;
+      else {
+        const int ex = (int)(amax >> 23);
+        const int fl = ex ? ex - 127 : (31 - __clz((int)amax)) - 149;
+        E = max(-127, fl - 2);
+      }
+      uint32_t pk[4];
+      if (E >= -126 && amax < 0x7F800000u) {
+        // the convert divides by 2^E exactly and rounds to nearest even
+        const float sc = bitsf((uint32_t)(E + 127) << 23);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w = 0;
+          static_for<0, 4>([&](auto ic) {
+            constexpr int b = decltype(ic)::value;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * q + 2 * b], x[8 * q + 2 * b + 1], sc, b);
+          });
+          pk[q] = clear_neg_zero(w);
+        }
+      } else {
+        typedef float f8v __attribute__((ext_vector_type(8)));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f8v xv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[i] = x[8 * q + i];
+          pk[q] = encode_mx_thresholds<8>(xv, E);
+        }
+      }
+      if (r < p.rows) {
+        *(uint4*)(p.codes + r * (p.cols / 2) + cj * (L / 2)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        p.scales[r * rpr + cj] = (uint8_t)(E + 127);
+      }
+    }
+  }
+}
+
+// grid for mx32_kernel: a thread count that is a multiple of the runs per row,
+// near the usual cap
+int mx32_grid(int64_t rows, int64_t rpr) {
+  int64_t a = rpr, b = kThreads;
+  while (b) { const int64_t t = a % b; a = b; b = t; }  // a = gcd(rpr, kThreads)
+  const int64_t base = rpr / a;                          // the fewest workgroups covering whole rows
+  // two rows per thread (one iteration of two rows in flight), at most 8
+  // workgroups per CU
+  const int64_t want = std::min<int64_t>((rows * rpr + 2 * kThreads - 1) / (2 * kThreads), 256 * 8);
+  return (int)std::max(base, want / base * base);
 }
 
 // ---------------------------------------------------------------- global amax
@@ -1124,6 +1329,15 @@ hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   }
   // the brute-force search is compute-bound: one addressing variant suffices
   const bool contig = RULE != BRUTE && p.ld == p.cols && p.chan_scale == nullptr;
+  if constexpr (FMT == NVFP4 && RULE != BRUTE && B >= 16) {
+    if (contig && p.fused_denom == 0.0f) {
+      // two runs per thread and iteration: at least one whole iteration each
+      const int g16 = grid_for((p.rows * (p.cols / 16) + 1) / 2);
+      if (bf16) hipLaunchKernelGGL((nv16_kernel<B, RULE, true>), dim3(g16), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((nv16_kernel<B, RULE, false>), dim3(g16), dim3(kThreads), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (contig) {
     if (bf16) hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, true, RULE != BRUTE>), dim3(grid), dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((quantize_kernel<FMT, B, RULE, false, RULE != BRUTE>), dim3(grid), dim3(kThreads), 0, s, p);
@@ -1178,7 +1392,21 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
     if (e != hipSuccess) return e;
   }
   switch (fmt) {
-    case MXFP4: return launch_q3<MXFP4, 32, ABSMAX>(bf16, q, s);
+    case MXFP4: {
+      const int64_t rpr = q.cols / 32;
+      const int grid = mx32_grid(q.rows, rpr);
+      const bool chan = q.chan_scale != nullptr, had = q.hadamard == 32;
+#define FP4Q_MX(BF, CH, HD) hipLaunchKernelGGL((mx32_kernel<BF, CH, HD>), dim3(grid), dim3(kThreads), 0, s, q)
+      if (bf16) {
+        if (chan) { if (had) FP4Q_MX(true, true, true); else FP4Q_MX(true, true, false); }
+        else { if (had) FP4Q_MX(true, false, true); else FP4Q_MX(true, false, false); }
+      } else {
+        if (chan) { if (had) FP4Q_MX(false, true, true); else FP4Q_MX(false, true, false); }
+        else { if (had) FP4Q_MX(false, false, true); else FP4Q_MX(false, false, false); }
+      }
+#undef FP4Q_MX
+      return hipGetLastError();
+    }
     case RAZER_A: return launch_q2<RAZER_A, ABSMAX>(block, bf16, q, s);
     case RAZER_W: return launch_q2<RAZER_W, ABSMAX>(block, bf16, q, s);
     default:

@@ -28,9 +28,10 @@
  *             RAZER_W  bits 7:6 = index into special[4], bits 5:0 = E3M3 code
  *   global  one FP32 on the device; an element decodes to value * scale * g.
  *
- * Ownership: the caller allocates and owns every buffer; libfp4q never
- * allocates or frees device memory and keeps no state beyond its loaded code.
- * Calls are thread-safe.
+ * Ownership: the caller allocates and owns every buffer it passes.  The only
+ * device memory libfp4q allocates itself is a split-K workspace of 32 MiB per
+ * (device, stream), taken with hipMalloc when fp4q_gemm_w4a4 first splits K on
+ * that stream and kept until the process ends.  Calls are thread-safe.
  *
  * Asynchrony: every call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t passed as void*, NULL = default stream)
@@ -143,7 +144,15 @@ fp4q_status fp4q_dequantize(const fp4q_quant_desc* desc, const uint8_t* codes,
 /*
  * W4A4 block-scaled matmul C = (g_a * g_w) * A^ W^T  with A^ (M x K) and W^
  * (N x K, row n = output channel) given as codes and scales; accumulation in
- * FP32; C = RN32(RN32(g_a*g_w) * acc), stored fp32 or bf16 (RNE), row pitch ldc.
+ * FP32; C = RN32(g * acc) with g = RN32(g_a*g_w), stored fp32 or bf16 (RNE of
+ * that FP32 value), row pitch ldc.  On launches with few output tiles the
+ * library may split K into S contiguous ranges with accumulators acc_0 ..
+ * acc_{S-1}; then C = (...((p_0 + p_1) + p_2) ... + p_{S-1}) with
+ * p_s = RN32(g * acc_s), each addition rounded to FP32, in that order, and
+ * stored as above.  S depends only on the shape, the formats and the device
+ * (S = 1 if the stream's workspace could not be allocated), so every launch of
+ * the same arguments gives the same bytes.  The summation order inside each
+ * acc_s is the kernel's and is not specified.
  * Pages: NVFP4 W4A4 -- "Why Gated DeltaNet Survives..." review, section 1;
  * RaZeR weight-activation GEMM -- RaZeR summary 2.3; MXFP4 W4A4 -- MACaQ
  * review, section 3.

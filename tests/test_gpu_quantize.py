@@ -263,3 +263,49 @@ def test_prefill_workload(B):
     sampled_parity(B, a, dev(a, bf16=True), "nvfp4", 16, "4over6", "given", sample_rows(32768, 64, 40), g_given=g)
     w = datagen.prefill_weight(5120)
     sampled_parity(B, w, dev(w), "nvfp4", 16, "4over6", "auto", sample_rows(5120, 64, 41))
+
+
+def test_tiny_workload_quantize_and_gemm(B):
+    # the tiny NVFP4 workload on its own tensors: W 256 x 256 under abs-max,
+    # 4-over-6 and brute force, A 64 x 256 under abs-max (block 16, E4M3, no
+    # global scale), all through the HIP quantizer byte for byte; then the
+    # W4A4 matmul of the HIP-produced codes against the oracle's matmul of the
+    # oracle's codes
+    import torch
+    from tests.gpu_util import rel_fro
+    d = datagen.tiny()
+    ag = dev(d["A"])
+    wg = dev(d["W"])
+    run_pair(B, d["A"], ag, "nvfp4", 16, "absmax", "none")
+    case("tiny workload: activation quantize")
+    ac, as_, _ = B.quantize(ag, "nvfp4", 16, "absmax", "none")
+    oac, oas, _ = O.quantize(d["A"], "nvfp4", 16, O.ABSMAX, O.G_NONE)
+    for rule, orule in (("absmax", O.ABSMAX), ("4over6", O.FOUR_OVER_SIX), ("brute", O.BRUTE)):
+        run_pair(B, d["W"], wg, "nvfp4", 16, rule, "none")
+        case(f"tiny workload: weight quantize {rule} and GEMM 64x256x256")
+        wc, ws, _ = B.quantize(wg, "nvfp4", 16, rule, "none")
+        c = B.gemm("nvfp4", ac, as_, None, "nvfp4", wc, ws, None)
+        torch.cuda.synchronize()
+        owc, ows, _ = O.quantize(d["W"], "nvfp4", 16, orule, O.G_NONE)
+        ref = O.gemm_rows("nvfp4", oac, oas, 1.0, "nvfp4", owc, ows, 1.0, None, 64, 256, 256)
+        assert rel_fro(host(c), ref) <= 1e-3
+
+
+def test_mxfp4_linear_device_channel_scale(B):
+    # the MXFP4 linear workload as the benchmark runs it: t and r from the
+    # device's channel-scale kernel (within one fp32 ulp of the oracle's; the
+    # binary64 column sums add in another order), then the quantizer at full
+    # size with those t and r; sampled rows against the oracle given the same
+    # t and r, byte for byte
+    import torch
+    d = datagen.mxfp4_linear()
+    xb, w = d["X_bf16"], d["W"]
+    t_or, r_or = O.channel_scale(xb, w, 0.75)
+    case("channel scale 4096 x 4096 bf16 with 14336 x 4096 fp32")
+    tg, rg = B.channel_scale(dev(xb, bf16=True), dev(w), 0.75)
+    torch.cuda.synchronize()
+    t, r = host(tg), host(rg)
+    assert np.max(np.abs(t.view(np.int32).astype(np.int64) - t_or.view(np.int32))) <= 1
+    assert np.max(np.abs(r.view(np.int32).astype(np.int64) - r_or.view(np.int32))) <= 2
+    sampled_parity(B, xb, dev(xb, bf16=True), "mxfp4", 32, "absmax", "none", sample_rows(4096, 64, 22), t=t, had=32)
+    sampled_parity(B, w, dev(w), "mxfp4", 32, "absmax", "none", sample_rows(14336, 64, 23), t=r, had=32)
