@@ -58,6 +58,8 @@ _SIGS = {
     "fp4q_quantize": (_int, [ctypes.POINTER(fp4q_quant_desc), _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "fp4q_dequantize": (_int, [ctypes.POINTER(fp4q_quant_desc), _vp, _vp, _vp, _i64, _i64, _vp, _int, _i64, _vp]),
     "fp4q_gemm_w4a4": (_int, [_int, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _i64, _vp]),
+    "fp4q_gemm_w4a4_noalloc": (_int, [_int, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
+                                      _i64, _vp]),
     "fp4q_channel_scale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp]),
     "fp4q_status_string": (ctypes.c_char_p, [_int]),
     "fp4q_abi_version": (_u32, []),
@@ -172,6 +174,17 @@ def fp4q_gemm_w4a4(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_glo
                                _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
                                ctypes.cast(sp, ctypes.c_void_p) if sp is not None else None,
                                M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a4")
+
+
+def fp4q_gemm_w4a4_noalloc(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_global, w_special,
+                           M: int, N: int, K: int, c, c_dtype: int, ldc: int, stream=None) -> None:
+    sp = None
+    if w_special is not None:
+        sp = (ctypes.c_float * 4)(*[float(v) for v in w_special])
+    _check(_lib.fp4q_gemm_w4a4_noalloc(_fmt(fa), _ptr(a_codes), _ptr(a_scales), _ptr(a_global), _fmt(fw),
+                                       _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                       ctypes.cast(sp, ctypes.c_void_p) if sp is not None else None,
+                                       M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a4_noalloc")
 
 
 def fp4q_channel_scale(x, x_dtype: int, rows_x: int, ldx: int, w, w_dtype: int, rows_w: int, ldw: int,

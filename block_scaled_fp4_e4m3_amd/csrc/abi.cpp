@@ -61,6 +61,45 @@ fp4q_status device_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4
 
 size_t elem_size(fp4q_dtype t) { return t == FP4Q_BF16 ? 2 : 4; }
 
+// Validation shared by the two matmul entry points, then the launch
+// parameters.  Touches no HIP API.
+fp4q_status gemm_params(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                        fp4q_format fw, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                        const float* w_special, int64_t M, int64_t N, int64_t K, void* c, fp4q_dtype c_dtype,
+                        int64_t ldc, GemmParams& p) {
+  if (!valid_format(fa) || !valid_format(fw)) return FP4Q_ERR_FORMAT;
+  if ((fa == FP4Q_MXFP4) != (fw == FP4Q_MXFP4) || fa == FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
+  if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
+  if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
+  const int64_t block = fa == FP4Q_MXFP4 ? 32 : 16;
+  if (M < 0 || N < 0 || K <= 0 || K % block != 0 || K > (int64_t(1) << 24) || ldc < N) return FP4Q_ERR_SHAPE;
+  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  if (tiles_n > 0 && tiles_m > INT32_MAX / tiles_n) return FP4Q_ERR_SHAPE;
+  if (fw == FP4Q_NVFP4_RAZER_W)
+    for (int i = 0; i < 4; ++i)
+      if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
+  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(c) ||
+      (ldc * (int64_t)elem_size(c_dtype)) % 16 != 0)
+    return FP4Q_ERR_ALIGN;
+  if ((a_global && ((uintptr_t)a_global & 3u)) || (w_global && ((uintptr_t)w_global & 3u)))
+    return FP4Q_ERR_ALIGN;
+  p.a_codes = a_codes;
+  p.a_scales = a_scales;
+  p.a_global = a_global;
+  p.w_codes = w_codes;
+  p.w_scales = w_scales;
+  p.w_global = w_global;
+  for (int i = 0; i < 4; ++i) p.w_special[i] = (fw == FP4Q_NVFP4_RAZER_W) ? w_special[i] : 0.0f;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  p.c_bf16 = c_dtype == FP4Q_BF16;
+  return FP4Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,38 +166,25 @@ fp4q_status fp4q_gemm_w4a4(fp4q_format fa, const uint8_t* a_codes, const uint8_t
                            const uint8_t* w_scales, const float* w_global,
                            const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
                            fp4q_dtype c_dtype, int64_t ldc, void* stream) {
-  if (!valid_format(fa) || !valid_format(fw)) return FP4Q_ERR_FORMAT;
-  if ((fa == FP4Q_MXFP4) != (fw == FP4Q_MXFP4) || fa == FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
-  if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
-  if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
-  if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
-  const int64_t block = fa == FP4Q_MXFP4 ? 32 : 16;
-  if (M < 0 || N < 0 || K <= 0 || K % block != 0 || K > (int64_t(1) << 24) || ldc < N) return FP4Q_ERR_SHAPE;
-  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
-  if (tiles_n > 0 && tiles_m > INT32_MAX / tiles_n) return FP4Q_ERR_SHAPE;
-  if (fw == FP4Q_NVFP4_RAZER_W)
-    for (int i = 0; i < 4; ++i)
-      if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
-  if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(c) ||
-      (ldc * (int64_t)elem_size(c_dtype)) % 16 != 0)
-    return FP4Q_ERR_ALIGN;
-  if ((a_global && ((uintptr_t)a_global & 3u)) || (w_global && ((uintptr_t)w_global & 3u)))
-    return FP4Q_ERR_ALIGN;
   GemmParams p{};
-  p.a_codes = a_codes;
-  p.a_scales = a_scales;
-  p.a_global = a_global;
-  p.w_codes = w_codes;
-  p.w_scales = w_scales;
-  p.w_global = w_global;
-  for (int i = 0; i < 4; ++i) p.w_special[i] = (fw == FP4Q_NVFP4_RAZER_W) ? w_special[i] : 0.0f;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.c = c;
-  p.ldc = ldc;
-  p.c_bf16 = c_dtype == FP4Q_BF16;
+  fp4q_status st = gemm_params(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_global, w_special, M, N,
+                               K, c, c_dtype, ldc, p);
+  if (st != FP4Q_OK || M == 0 || N == 0) return st;
   return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{nullptr, kSplitWorkspaceBytes}));
+}
+
+fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const float* a_global, fp4q_format fw, const uint8_t* w_codes,
+                                   const uint8_t* w_scales, const float* w_global,
+                                   const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
+                                   fp4q_dtype c_dtype, int64_t ldc, void* stream) {
+  GemmParams p{};
+  fp4q_status st = gemm_params(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_global, w_special, M, N,
+                               K, c, c_dtype, ldc, p);
+  if (st != FP4Q_OK || M == 0 || N == 0) return st;
+  float* scratch = noalloc_scratch();
+  if (!scratch) return FP4Q_ERR_DEVICE;
+  return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{scratch, kSplitWorkspaceBytes}));
 }
 
 fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x, int64_t ldx,

@@ -72,6 +72,9 @@ hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s, const
 // the split-K workspace of stream s on the current device (allocated on first
 // use, kept until the process ends), or nullptr
 float* split_workspace(hipStream_t s);
+// the device address of the library's own split-K array on the current
+// device (looked up once per device), or nullptr if the lookup failed
+float* noalloc_scratch();
 hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s);
 
 // compile-time loop: f(std::integral_constant<int, I>) for I in [B, E); used

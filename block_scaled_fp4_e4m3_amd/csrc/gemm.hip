@@ -1720,6 +1720,32 @@ float* split_workspace(hipStream_t s) {
   return (float*)ptr;
 }
 
+// Split-K scratch of the non-allocating matmul entry point: one array per
+// device, part of the loaded code object, held until the process ends and
+// shared by every call of that entry point on the device (calls that overlap
+// on one device race on it).  Host code never uses the name itself, which on
+// the host is only a stand-in: it uses the device address looked up below.
+__device__ __align__(256) uint8_t scratch[kSplitWorkspaceBytes];
+
+float* noalloc_scratch() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  static bool looked_up[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!looked_up[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      ptr = nullptr;
+    }
+    addr[dev] = ptr;
+    looked_up[dev] = true;
+  }
+  return (float*)addr[dev];
+}
+
 hipError_t launch_gemm(int fa, int fw, const GemmParams& p0, hipStream_t s, const Workspace& ws) {
   if (p0.M == 0 || p0.N == 0) return hipSuccess;
   GemmParams p = p0;

@@ -175,6 +175,26 @@ fp4q_status fp4q_gemm_w4a4(fp4q_format fa, const uint8_t* a_codes, const uint8_t
                            fp4q_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * fp4q_gemm_w4a4 for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, checks, kernels and result -- the same bytes as fp4q_gemm_w4a4 --
+ * but the partial results of K splits go to an array that is part of the
+ * library's code object, 32 MiB per device, instead of a per-stream workspace.
+ * It calls no allocating routine.  Its device address is looked up on the
+ * first call on each device (FP4Q_ERR_DEVICE if that fails).  The split count
+ * is capped so that the partials fit the array, the same cap fp4q_gemm_w4a4
+ * applies to its workspace, so no shape needs more than the array holds.
+ * Every call on a device shares that device's array, and nothing in it has to
+ * start at zero; calls that overlap on one device (on different streams, or
+ * from several threads) race on it and must be ordered by the caller.
+ */
+fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const float* a_global, fp4q_format fw, const uint8_t* w_codes,
+                                   const uint8_t* w_scales, const float* w_global,
+                                   const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
+                                   fp4q_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
  * Per-channel scale of MACaQ's online scaling (MACaQ review, section 3):
  *   t_j = (rms_j(W) / rms_j(X))^alpha, r_j = RN32(1 / t_j),
  * rms over the rows of each column, computed in binary64 and rounded to fp32;

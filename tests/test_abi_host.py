@@ -76,6 +76,7 @@ vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 L.fp4q_quantize.argtypes = [ctypes.POINTER(Desc), vp, ci, i64, i64, i64, vp, vp, vp, vp]
 L.fp4q_dequantize.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, i64, vp, ci, i64, vp]
 L.fp4q_gemm_w4a4.argtypes = [ci, vp, vp, vp, ci, vp, vp, vp, vp, i64, i64, i64, vp, ci, i64, vp]
+L.fp4q_gemm_w4a4_noalloc.argtypes = L.fp4q_gemm_w4a4.argtypes
 L.fp4q_channel_scale.argtypes = [vp, ci, i64, i64, vp, ci, i64, i64, i64, ctypes.c_double, vp, vp, vp]
 P = 0x100000  # aligned fake device address; never dereferenced on any error path
 
@@ -101,6 +102,9 @@ def dq(d=None, codes=P, scales=P, g=None, rows=4, cols=64, out=P, ot=0, ld=64):
 SP = (ctypes.c_float * 4)(5.0, -5.0, 2.5, -2.5)
 def gm(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc=8):
     return L.fp4q_gemm_w4a4(fa, a, sa, None, fw, w, sw, None, sp, M, N, K, c, ct, ldc, None)
+
+def gn(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc=8):
+    return L.fp4q_gemm_w4a4_noalloc(fa, a, sa, None, fw, w, sw, None, sp, M, N, K, c, ct, ldc, None)
 
 def cs(x=P, rows_x=4, ldx=8, w=P, rows_w=4, ldw=8, cols=8, alpha=0.75, t=P, r=P):
     return L.fp4q_channel_scale(x, 0, rows_x, ldx, w, 0, rows_w, ldw, cols, alpha, t, r, None)
@@ -141,6 +145,9 @@ res = {
  "g_ldc_align": gm(ldc=9), "g_dtype": gm(ct=3), "g_K_big": gm(K=(1 << 24) + 16),
  "g_tiles": gm(M=1 << 40, N=1 << 40, ldc=1 << 40),
  "g_bad_special": gm(fw=3, sp=ctypes.cast((ctypes.c_float * 4)(5.0, -5.0, 3.0, -2.5), vp)),
+ # the non-allocating matmul: the same checks
+ "gn_null_a": gn(a=None), "gn_mixed": gn(fa=1, fw=0), "gn_K_block": gn(K=24), "gn_align": gn(c=P + 4),
+ "gn_dtype": gn(ct=3),
  # channel scale
  "c_null": cs(t=None), "c_rows": cs(rows_x=0), "c_ld": cs(ldx=4), "c_alpha": cs(alpha=float("inf")),
 }
@@ -161,6 +168,7 @@ EXPECTED = {
     "g_null_a": 1, "g_null_c": 1, "g_null_special": 1, "g_mixed": 4, "g_razer_w_a": 4, "g_bad_format": 4,
     "g_K_block": 2, "g_K_mx": 2, "g_K_zero": 2, "g_M_neg": 2, "g_ldc": 2, "g_align": 3, "g_ldc_align": 3,
     "g_dtype": 5, "g_bad_special": 5, "g_K_big": 2, "g_tiles": 2,
+    "gn_null_a": 1, "gn_mixed": 4, "gn_K_block": 2, "gn_align": 3, "gn_dtype": 5,
     "c_null": 1, "c_rows": 2, "c_ld": 2, "c_alpha": 5,
 }
 
@@ -180,8 +188,8 @@ def test_zero_rows_and_empty_gemm_enqueue_nothing():
     # with no visible device
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     code = f"ROOT = {ROOT!r}\nLIB = {LIB!r}\n" + CHILD.split("res = {")[0] + textwrap.dedent('''
-print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0))
+print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0))
 ''')
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == ["0", "0", "0", "0", "0"]
+    assert out.stdout.split() == ["0", "0", "0", "0", "0", "0"]
