@@ -28,15 +28,16 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ---- constants (fp4q.h) -------------------------------------------------------
 FP4Q_OK, FP4Q_ERR_NULL, FP4Q_ERR_SHAPE, FP4Q_ERR_ALIGN = 0, 1, 2, 3
 FP4Q_ERR_FORMAT, FP4Q_ERR_ARG, FP4Q_ERR_UNSUPPORTED, FP4Q_ERR_DEVICE = 4, 5, 6, 7
-FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_NVFP4_RAZER_A, FP4Q_NVFP4_RAZER_W = 0, 1, 2, 3
+FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_NVFP4_RAZER_A, FP4Q_NVFP4_RAZER_W, FP4Q_UE5M3 = 0, 1, 2, 3, 4
 FP4Q_F32, FP4Q_BF16 = 0, 1
-FP4Q_RULE_ABSMAX, FP4Q_RULE_4OVER6, FP4Q_RULE_BRUTE = 0, 1, 2
+FP4Q_RULE_ABSMAX, FP4Q_RULE_4OVER6, FP4Q_RULE_BRUTE, FP4Q_RULE_EXPSEARCH = 0, 1, 2, 3
 FP4Q_FLAG_PREVENT_ZERO = 0x100
 FP4Q_GLOBAL_NONE, FP4Q_GLOBAL_AUTO, FP4Q_GLOBAL_GIVEN = 0, 1, 2
 
 FORMATS = {"nvfp4": FP4Q_NVFP4, "mxfp4": FP4Q_MXFP4, "razer_a": FP4Q_NVFP4_RAZER_A,
-           "razer_w": FP4Q_NVFP4_RAZER_W}
-RULES = {"absmax": FP4Q_RULE_ABSMAX, "4over6": FP4Q_RULE_4OVER6, "brute": FP4Q_RULE_BRUTE}
+           "razer_w": FP4Q_NVFP4_RAZER_W, "ue5m3": FP4Q_UE5M3}
+RULES = {"absmax": FP4Q_RULE_ABSMAX, "4over6": FP4Q_RULE_4OVER6, "brute": FP4Q_RULE_BRUTE,
+         "expsearch": FP4Q_RULE_EXPSEARCH}
 GLOBAL_MODES = {"none": FP4Q_GLOBAL_NONE, "auto": FP4Q_GLOBAL_AUTO, "given": FP4Q_GLOBAL_GIVEN}
 
 

@@ -16,7 +16,9 @@ using namespace fp4q;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_format(int f) { return f >= FP4Q_NVFP4 && f <= FP4Q_NVFP4_RAZER_W; }
+bool valid_format(int f) { return f >= FP4Q_NVFP4 && f <= FP4Q_UE5M3; }
+// formats the matmul consumes (UE5M3 is quantize/dequantize only)
+bool gemm_format(int f) { return f >= FP4Q_NVFP4 && f <= FP4Q_NVFP4_RAZER_W; }
 
 // RaZeR special value: multiple of 0.5 (RaZeR summary 2.2), 0 < |v| <= 7.5 so
 // that value * scale stays exact in the matmul's f16 decode, and not one of
@@ -48,12 +50,23 @@ fp4q_status check_desc(const fp4q_quant_desc* d, bool quantizing) {
   if (!quantizing) return FP4Q_OK;
   const uint32_t rule = d->rule & 0xFFu, flags = d->rule & ~0xFFu;
   if (flags & ~(uint32_t)FP4Q_FLAG_PREVENT_ZERO) return FP4Q_ERR_ARG;
-  if (rule > FP4Q_RULE_BRUTE) return FP4Q_ERR_ARG;
-  if (d->format != FP4Q_NVFP4 && rule != FP4Q_RULE_ABSMAX) return FP4Q_ERR_ARG;
+  if (rule > FP4Q_RULE_EXPSEARCH) return FP4Q_ERR_ARG;
+  switch (d->format) {
+    case FP4Q_NVFP4:
+    case FP4Q_UE5M3:
+      if (rule > FP4Q_RULE_BRUTE) return FP4Q_ERR_ARG;
+      break;
+    case FP4Q_MXFP4:
+      if (rule != FP4Q_RULE_ABSMAX && rule != FP4Q_RULE_EXPSEARCH) return FP4Q_ERR_ARG;
+      break;
+    default:  // RaZeR: abs-max scale, the special value by block error
+      if (rule != FP4Q_RULE_ABSMAX) return FP4Q_ERR_ARG;
+  }
   if (d->format == FP4Q_MXFP4 && flags) return FP4Q_ERR_ARG;
   if (d->global_mode < FP4Q_GLOBAL_NONE || d->global_mode > FP4Q_GLOBAL_GIVEN) return FP4Q_ERR_ARG;
   if (d->format == FP4Q_MXFP4 && d->global_mode != FP4Q_GLOBAL_NONE) return FP4Q_ERR_ARG;
-  if (d->hadamard != 0 && d->hadamard != 32) return FP4Q_ERR_ARG;
+  if (d->format == FP4Q_UE5M3 && d->global_mode == FP4Q_GLOBAL_AUTO) return FP4Q_ERR_ARG;
+  if (d->hadamard != 0 && d->hadamard != 16 && d->hadamard != 32) return FP4Q_ERR_ARG;
   return FP4Q_OK;
 }
 
@@ -67,7 +80,7 @@ fp4q_status gemm_params(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a
                         fp4q_format fw, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                         const float* w_special, int64_t M, int64_t N, int64_t K, void* c, fp4q_dtype c_dtype,
                         int64_t ldc, GemmParams& p) {
-  if (!valid_format(fa) || !valid_format(fw)) return FP4Q_ERR_FORMAT;
+  if (!gemm_format(fa) || !gemm_format(fw)) return FP4Q_ERR_FORMAT;
   if ((fa == FP4Q_MXFP4) != (fw == FP4Q_MXFP4) || fa == FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
   if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
   if (!a_codes || !a_scales || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
@@ -113,7 +126,7 @@ fp4q_status fp4q_quantize(const fp4q_quant_desc* desc, const void* x, fp4q_dtype
   if (!x || !codes || !scales) return FP4Q_ERR_NULL;
   if (desc->global_mode != FP4Q_GLOBAL_NONE && !global) return FP4Q_ERR_NULL;
   if (rows < 0 || cols <= 0 || ld_x < cols || cols % desc->block != 0) return FP4Q_ERR_SHAPE;
-  if (desc->hadamard == 32 && cols % 32 != 0) return FP4Q_ERR_SHAPE;
+  if (desc->hadamard != 0 && cols % desc->hadamard != 0) return FP4Q_ERR_SHAPE;
   if (!aligned16(x) || (ld_x * (int64_t)elem_size(x_dtype)) % 16 != 0 || !aligned16(codes))
     return FP4Q_ERR_ALIGN;
   if (desc->chan_scale && !aligned16(desc->chan_scale)) return FP4Q_ERR_ALIGN;

@@ -8,8 +8,8 @@
 
 namespace fp4q {
 
-enum Fmt : int { NVFP4 = 0, MXFP4 = 1, RAZER_A = 2, RAZER_W = 3 };
-enum Rule : int { ABSMAX = 0, FOUR6 = 1, BRUTE = 2 };
+enum Fmt : int { NVFP4 = 0, MXFP4 = 1, RAZER_A = 2, RAZER_W = 3, UE5M3 = 4 };
+enum Rule : int { ABSMAX = 0, FOUR6 = 1, BRUTE = 2, EXPSEARCH = 3 };
 enum GMode : int { G_NONE = 0, G_AUTO = 1, G_GIVEN = 2 };
 
 struct QuantParams {
@@ -20,7 +20,7 @@ struct QuantParams {
   uint8_t* scales;        // rows x cols/block
   float* global;          // device scalar or nullptr (= 1.0)
   const float* chan_scale;// device, cols, or nullptr
-  int hadamard;           // 0 or 32
+  int hadamard;           // 0, 16 or 32
   int prevent_zero;
   float special[4];       // RAZER_W table
   float fused_denom;      // > 0: one workgroup that first sets *global = amax / fused_denom (automatic g)

@@ -72,12 +72,15 @@ __device__ __forceinline__ uint32_t ru_bits(double T) {
 }
 
 // scale-format values (binary64, exact)
-template <int SF>  // 0: E4M3 (codes 0..126), 1: E3M3 (codes 0..63)
+template <int SF>  // 0: E4M3 (codes 0..126), 1: E3M3 (codes 0..63), 2: UE5M3 (codes 0..255)
 __device__ __forceinline__ double sf_val(int k) {
   int e = k >> 3, m = k & 7;
   if (SF == 0) return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
-  return e == 0 ? ldexp((double)m, -5) : ldexp((double)(8 + m), e - 6);
+  if (SF == 1) return e == 0 ? ldexp((double)m, -5) : ldexp((double)(8 + m), e - 6);
+  return e == 0 ? ldexp((double)m, -17) : ldexp((double)(8 + m), e - 18);
 }
+template <int SF>
+constexpr int sf_kmax() { return SF == 0 ? 126 : SF == 1 ? 63 : 255; }
 
 // E2M1 magnitudes and the midpoints between neighbours
 // (compile-time arrays, indexed with constants only: literals, no memory loads)
@@ -89,6 +92,7 @@ template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<NVFP4>   { static constexpr int SF = 0, KMAX = 126, NSP = 0; };
 template <> struct FmtTraits<RAZER_A> { static constexpr int SF = 0; };
 template <> struct FmtTraits<RAZER_W> { static constexpr int SF = 1, KMAX = 63,  NSP = 4; };
+template <> struct FmtTraits<UE5M3>   { static constexpr int SF = 2, KMAX = 255, NSP = 0; };
 
 // LDS tables, built once per workgroup for the launch's global scale g
 template <int FMT>
@@ -160,25 +164,20 @@ __device__ void build_tables(Tables<FMT>& T, float g, const float* special) {
 // scale code guess for a/(T g) in binary64, off by at most one
 template <int SF>
 __device__ __forceinline__ int select_scale_guess(float a, double inv_Tg) {
-  constexpr int KMAX = SF == 0 ? 126 : 63;
+  constexpr int KMAX = sf_kmax<SF>();
+  // largest value, smallest normal, subnormal quantum (as a power of two), bias
+  constexpr double MAXV = SF == 0 ? 448.0 : SF == 1 ? 30.0 : 122880.0;
+  constexpr double MINN = SF == 0 ? 0.015625 : SF == 1 ? 0.25 : 0x1p-14;
+  constexpr double SUBQ = SF == 0 ? 512.0 : SF == 1 ? 32.0 : 131072.0;
+  constexpr int BIAS = SF == 0 ? 7 : SF == 1 ? 3 : 15;
   double y = (double)a * inv_Tg;
   int k;
-  if (SF == 0) {
-    if (!(y < 448.0)) k = KMAX;
-    else if (y < 0.015625) k = (int)(y * 512.0);
-    else {
-      uint64_t b = (uint64_t)__double_as_longlong(y);
-      int e = (int)((b >> 52) & 0x7FF) - 1023;
-      k = ((e + 7) << 3) | (int)((b >> 49) & 7);
-    }
-  } else {
-    if (!(y < 30.0)) k = KMAX;
-    else if (y < 0.25) k = (int)(y * 32.0);
-    else {
-      uint64_t b = (uint64_t)__double_as_longlong(y);
-      int e = (int)((b >> 52) & 0x7FF) - 1023;
-      k = ((e + 3) << 3) | (int)((b >> 49) & 7);
-    }
+  if (!(y < MAXV)) k = KMAX;
+  else if (y < MINN) k = (int)(y * SUBQ);
+  else {
+    uint64_t b = (uint64_t)__double_as_longlong(y);
+    int e = (int)((b >> 52) & 0x7FF) - 1023;
+    k = ((e + BIAS) << 3) | (int)((b >> 49) & 7);
   }
   return k;
 }
@@ -186,7 +185,7 @@ __device__ __forceinline__ int select_scale_guess(float a, double inv_Tg) {
 // nearest scale code to a/(T g) from the midpoint table
 template <int SF>
 __device__ __forceinline__ int select_scale(float a, const uint32_t* smid, double inv_Tg) {
-  constexpr int KMAX = SF == 0 ? 126 : 63;
+  constexpr int KMAX = sf_kmax<SF>();
   int k = select_scale_guess<SF>(a, inv_Tg);
   uint32_t ab = fbits(a);
   if (k < KMAX && ab > smid[k]) ++k;
@@ -277,11 +276,46 @@ __device__ __forceinline__ void load_raw(const QuantParams& p, int64_t r, int64_
   }
 }
 
-// widen a raw chunk, apply the channel scale and the size-32 block-Hadamard
-// (lanes of a 32-group are adjacent)
+// Block-Hadamard of size HS (16 or 32) over a lane's L consecutive elements
+// and, when HS > L, its neighbours' (the HS / L lanes of a group are
+// adjacent): the natural-order FWHT, in-lane stages h < L, then cross-lane
+// stages with partner lane ^ (h / L); then the orthonormal factor
+// RN32(2^-2.5) for 32, exactly 1/4 for 16.
+template <int L, int HS>
+__device__ __forceinline__ void block_hadamard(float* x) {
+#pragma unroll
+  for (int h = 1; h < L && h < HS; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if ((i & h) == 0) {
+        float u = x[i], w = x[i + h];
+        x[i] = u + w;
+        x[i + h] = u - w;
+      }
+    }
+  }
+  // butterfly with the partner lane: the lower lane keeps x + o, the upper
+  // o - x, written as o + (+-x) (the same IEEE operations)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < HS / L; d *= 2) {
+    const uint32_t neg = (lane & d) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const float o = lane_xor_f(x[i], d);
+      x[i] = o + bitsf(fbits(x[i]) ^ neg);
+    }
+  }
+  const float c = HS == 32 ? bitsf(0x3E3504F3u) : 0.25f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) x[i] = x[i] * c;
+}
+
+// widen a raw chunk, apply the channel scale and the block-Hadamard of size
+// had (0, 16 or 32)
 template <int L, bool BF16, bool PRE_T = false>
 __device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, const Raw<L, BF16>& raw, float* x,
-                                             bool chan, bool had) {
+                                             bool chan, int had) {
   if constexpr (BF16) {
 #pragma unroll
     for (int i = 0; i < L / 2; ++i) {
@@ -304,41 +338,13 @@ __device__ __forceinline__ void finish_chunk(const QuantParams& p, int64_t j0, c
       }
     }
   }
-  if (had) {
-    // in-lane stages h < L
-#pragma unroll
-    for (int h = 1; h < L; h *= 2) {
-#pragma unroll
-      for (int i = 0; i < L; ++i) {
-        if ((i & h) == 0) {
-          float u = x[i], w = x[i + h];
-          x[i] = u + w;
-          x[i + h] = u - w;
-        }
-      }
-    }
-    // cross-lane stages h = L .. 16 with partner lane ^ (h / L)
-    // butterfly with the partner lane: the lower lane keeps x + o, the upper
-    // o - x, written as o + (+-x) (the same IEEE operations)
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 32 / L; d *= 2) {
-      const uint32_t neg = (lane & d) ? 0x80000000u : 0u;
-#pragma unroll
-      for (int i = 0; i < L; ++i) {
-        const float o = lane_xor_f(x[i], d);
-        x[i] = o + bitsf(fbits(x[i]) ^ neg);
-      }
-    }
-    const float c = bitsf(0x3E3504F3u);  // RN32(2^-2.5)
-#pragma unroll
-    for (int i = 0; i < L; ++i) x[i] = x[i] * c;
-  }
+  if (had == 32) block_hadamard<L, 32>(x);
+  else if (had == 16) block_hadamard<L, 16>(x);
 }
 
 template <int L, bool BF16>
 __device__ __forceinline__ void load_chunk(const QuantParams& p, int64_t r, int64_t j0, float* x,
-                                           bool chan, bool had) {
+                                           bool chan, int had) {
   Raw<L, BF16> raw;
   load_raw<L, BF16>(p, r, j0, raw);
   finish_chunk<L, BF16>(p, j0, raw, x, chan, had);
@@ -393,6 +399,14 @@ __device__ __forceinline__ uint32_t encode_special(const float* x, const uint32_
 // E4M3 scale code (0..126) -> its value as FP32: the hardware FP8 decode
 // (OCP E4M3, exact) with unit scale
 __device__ __forceinline__ float e4m3_f32(int k) { return __builtin_amdgcn_cvt_scalef32_f32_fp8(k, 1.0f, 0); }
+// UE5M3 scale code (0..255) -> its value as FP32 (exact: every value is a
+// normal FP32 number)
+__device__ __forceinline__ float ue5m3_f32(int k) {
+  const int e = k >> 3, m = k & 7;
+  return e == 0 ? (float)m * 0x1p-17f : bitsf((uint32_t)(e + 112) << 23 | (uint32_t)m << 20);
+}
+template <int SF>
+__device__ __forceinline__ float sf_f32(int k) { return SF == 0 ? e4m3_f32(k) : ue5m3_f32(k); }
 
 // codes whose magnitude rounded to 0 carry the sign of x in the hardware
 // convert (code 0x8); the format writes them as 0
@@ -422,23 +436,30 @@ __device__ __forceinline__ int rtn_count(uint32_t xb, const uint32_t t[7]) {
   return m;
 }
 
-// element thresholds of E4M3 scale code k under g, formed in binary64 (the
-// same values the LDS tables hold)
+// element thresholds of scale code k (format SF) under g, formed in binary64
+// (the same values the LDS tables hold)
+template <int SF>
 __device__ __forceinline__ void nv_thresholds(int k, double gd, uint32_t t[7]) {
-  const double sv = sf_val<0>(k) * gd;
+  const double sv = sf_val<SF>(k) * gd;
 #pragma unroll
   for (int j = 0; j < 7; ++j) t[j] = k > 0 ? thr_bits((double)kMidD[j] * sv, (j & 1) != 0) : 0x7F800000u;
 }
 
-// nearest E4M3 code to a / (T g) (T = 6 or 4), ties to the even code,
-// saturating at 126: binary64 guess corrected by the exact scale midpoints
-__device__ __forceinline__ int select_e4m3_exact(float a, double inv_Tg, double Tg) {
-  int k = select_scale_guess<0>(a, inv_Tg);
+// nearest code of scale format SF to a / (T g) (T = 6 or 4), ties to the
+// even code, saturating at the largest: binary64 guess corrected by the exact
+// scale midpoints
+template <int SF>
+__device__ __forceinline__ int select_sf_exact(float a, double inv_Tg, double Tg) {
+  constexpr int KMAX = sf_kmax<SF>();
+  int k = select_scale_guess<SF>(a, inv_Tg);
   const uint32_t ab = fbits(a);
-  auto mid = [&](int j) { return thr_bits(0.5 * (sf_val<0>(j) + sf_val<0>(j + 1)) * Tg, (j & 1) != 0); };
-  if (k < 126 && ab > mid(k)) ++k;
+  auto mid = [&](int j) { return thr_bits(0.5 * (sf_val<SF>(j) + sf_val<SF>(j + 1)) * Tg, (j & 1) != 0); };
+  if (k < KMAX && ab > mid(k)) ++k;
   else if (k > 0 && ab <= mid(k - 1)) --k;
   return k;
+}
+__device__ __forceinline__ int select_e4m3_exact(float a, double inv_Tg, double Tg) {
+  return select_sf_exact<0>(a, inv_Tg, Tg);
 }
 
 // Exact side of a rounding midpoint.  The midpoint threshold is T = Q g
@@ -475,11 +496,11 @@ __device__ __attribute__((noinline)) uint32_t encode_mx_thresholds(float __attri
 // NVFP4 codes by the exact threshold search (a wave with a non-finite block,
 // or s g near the ends of the FP32 range).  Kept out of line: inlined, its
 // 7 x L comparison masks claim the scalar registers of the whole kernel.
-template <int L>
+template <int L, int SF = 0>
 __device__ __attribute__((noinline)) uint32_t encode_nv_thresholds(float __attribute__((ext_vector_type(L))) x, int k,
                                                                    float g) {
   uint32_t t[7];
-  nv_thresholds(k, (double)g, t);
+  nv_thresholds<SF>(k, (double)g, t);
   uint32_t plo = 0;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
@@ -529,7 +550,7 @@ __device__ __attribute__((noinline)) uint32_t resolve_ambiguous(float __attribut
 // that way, the whole wave resolves its ambiguous elements exactly.  The
 // bracket is used only for finite blocks with s g well inside the normal
 // range; a wave with any other block takes the threshold search.
-template <int L, int LPB>
+template <int L, int LPB, int SF = 0>
 __device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, float g, bool finite) {
   const float sg = s * g;
   const float r = __builtin_amdgcn_rcpf(sg);  // within 1 ulp of 1 / RN(s g)
@@ -547,7 +568,7 @@ __device__ __forceinline__ uint32_t encode_nv(const float* x, int k, float s, fl
 #pragma unroll
     for (int i = 0; i < L; ++i) xv[i] = x[i];
     if (wave_all(ok)) plo = resolve_ambiguous<L>(xv, plo, phi, s, g);
-    else return encode_nv_thresholds<L>(xv, k, g);
+    else return encode_nv_thresholds<L, SF>(xv, k, g);
   }
   return clear_neg_zero(plo);
 }
@@ -611,7 +632,7 @@ template <int L, bool BF16>
 __device__ float fused_auto_global(const QuantParams& p) {
   __shared__ uint32_t part[kThreads / 64];
   const bool chan = p.chan_scale != nullptr;
-  const bool had = p.hadamard == 32;
+  const int had = p.hadamard;
   const int64_t cpr = p.cols / L;
   const int64_t total = p.rows * cpr;
   uint32_t m = 0;
@@ -671,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   }
 
   const bool chan = p.chan_scale != nullptr;
-  const bool had = p.hadamard == 32;
+  const int had = p.hadamard;
   const int64_t cpr = p.cols / L;            // chunks per row
   const int64_t total = p.rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -735,25 +756,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
     uint32_t packed;
     uint8_t sbyte;
-    if constexpr (FMT == NVFP4) {
+    if constexpr (FMT == NVFP4 || FMT == UE5M3) {
       if constexpr (RULE == BRUTE) {
-        // every positive E4M3 scale; strict minimum, ties keep the smaller code
+        // every positive scale of the format; strict minimum, ties keep the
+        // smaller code
         float best = 0.f;
         int bestk = 1;
         packed = 0;
-        for (int k = 1; k <= 126; ++k) {
+        for (int k = 1; k <= FmtTraits<FMT>::KMAX; ++k) {
           uint32_t t[7];
 #pragma unroll
           for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
           uint32_t pk = encode_plain<L>(x, t);
-          float e = group_sum<LPB>(lane_sse<L>(x, pk, (float)sf_val<0>(k), g, false, 0.f));
+          float e = group_sum<LPB>(lane_sse<L>(x, pk, (float)sf_val<SF>(k), g, false, 0.f));
           if (k == 1 || e < best) { best = e; bestk = k; packed = pk; }
         }
         sbyte = (uint8_t)bestk;
       } else {
         const bool finite = amax < 0x7F800000u;
         int k6 = 0, k4 = 0;
-        if (wave_all(fast_scale && finite)) {
+        if (FMT == NVFP4 && wave_all(fast_scale && finite)) {
           typedef short s2v __attribute__((ext_vector_type(2)));
           const float a = bitsf(amax);
           const s2v z = {0, 0};
@@ -762,17 +784,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
           k6 = e4m3_from_low(wl & 0xFFu, a, 6.0f, g);
           if constexpr (RULE == FOUR6) k4 = e4m3_from_low(wl >> 8, a, 4.0f, g);
         } else {
-          k6 = select_e4m3_exact(bitsf(amax), inv6, 6.0 * (double)g);
-          if constexpr (RULE == FOUR6) k4 = select_e4m3_exact(bitsf(amax), inv4, 4.0 * (double)g);
+          // UE5M3 has no hardware convert; E4M3 outside the convert's range
+          k6 = select_sf_exact<SF>(bitsf(amax), inv6, 6.0 * (double)g);
+          if constexpr (RULE == FOUR6) k4 = select_sf_exact<SF>(bitsf(amax), inv4, 4.0 * (double)g);
         }
         if (p.prevent_zero && k6 == 0) k6 = 1;
-        const float s6 = e4m3_f32(k6);
-        packed = encode_nv<L, LPB>(x, k6, s6, g, finite);
+        const float s6 = sf_f32<SF>(k6);
+        packed = encode_nv<L, LPB, SF>(x, k6, s6, g, finite);
         sbyte = (uint8_t)k6;
         if constexpr (RULE == FOUR6) {
           if (p.prevent_zero && k4 == 0) k4 = 1;
-          const float s4 = e4m3_f32(k4);
-          uint32_t pk4 = encode_nv<L, LPB>(x, k4, s4, g, finite);
+          const float s4 = sf_f32<SF>(k4);
+          uint32_t pk4 = encode_nv<L, LPB, SF>(x, k4, s4, g, finite);
           float e6 = group_sum<LPB>(lane_sse<L>(x, packed, s6, g, false, 0.f));
           float e4 = group_sum<LPB>(lane_sse<L>(x, pk4, s4, g, false, 0.f));
           if (e4 < e6) { packed = pk4; sbyte = (uint8_t)k4; }
@@ -871,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 // kernel: tree(16) = tree(first 8) + tree(last 8).
 
 // codes of 16 elements as two words (elements 0-7, 8-15), -0 not yet cleared
-template <int LPB>
+template <int LPB, int SF = 0>
 __device__ __forceinline__ uint2 encode_nv16(const float* x, int k, float s, float g, bool finite) {
   const float sg = s * g;
   const float r = __builtin_amdgcn_rcpf(sg);  // within 1 ulp of 1 / RN(s g)
@@ -894,8 +917,8 @@ __device__ __forceinline__ uint2 encode_nv16(const float* x, int k, float s, flo
       l0 = resolve_ambiguous<8>(xa, l0, h0, s, g);
       l1 = resolve_ambiguous<8>(xb, l1, h1, s, g);
     } else {
-      l0 = encode_nv_thresholds<8>(xa, k, g);
-      l1 = encode_nv_thresholds<8>(xb, k, g);
+      l0 = encode_nv_thresholds<8, SF>(xa, k, g);
+      l1 = encode_nv_thresholds<8, SF>(xb, k, g);
     }
   }
   return make_uint2(l0, l1);
@@ -906,12 +929,13 @@ __device__ __forceinline__ float lane_sse16(const float* x, uint2 c, float s, fl
   return lane_sse<8>(x, c.x, s, g, false, 0.f) + lane_sse<8>(x + 8, c.y, s, g, false, 0.f);
 }
 
-template <int B, int RULE, bool BF16>
+template <int FMT, int B, int RULE, bool BF16>
 __global__ __launch_bounds__(kThreads) void nv16_kernel(QuantParams p) {
   constexpr int L = 16, LPB = B / L;
+  constexpr int SF = FmtTraits<FMT>::SF;
   static_assert(LPB == 1 || LPB == 2, "blocks of 16 or 32");
   const float g = p.global ? *p.global : 1.0f;
-  const bool had = p.hadamard == 32;
+  const int had = p.hadamard;
   const int64_t total = p.rows * (p.cols / L);  // runs
   const double inv6 = 1.0 / (6.0 * (double)g);
   const double inv4 = 1.0 / (4.0 * (double)g);
@@ -948,7 +972,7 @@ __global__ __launch_bounds__(kThreads) void nv16_kernel(QuantParams p) {
       amax = group_max<LPB>(amax);
       const bool finite = amax < 0x7F800000u;
       int k6 = 0, k4 = 0;
-      if (wave_all(fast_scale && finite)) {
+      if (FMT == NVFP4 && wave_all(fast_scale && finite)) {
         typedef short s2v __attribute__((ext_vector_type(2)));
         const float a = bitsf(amax);
         const s2v z = {0, 0};
@@ -957,17 +981,18 @@ __global__ __launch_bounds__(kThreads) void nv16_kernel(QuantParams p) {
         k6 = e4m3_from_low(wl & 0xFFu, a, 6.0f, g);
         if constexpr (RULE == FOUR6) k4 = e4m3_from_low(wl >> 8, a, 4.0f, g);
       } else {
-        k6 = select_e4m3_exact(bitsf(amax), inv6, 6.0 * (double)g);
-        if constexpr (RULE == FOUR6) k4 = select_e4m3_exact(bitsf(amax), inv4, 4.0 * (double)g);
+        // UE5M3 has no hardware convert; E4M3 outside the convert's range
+        k6 = select_sf_exact<SF>(bitsf(amax), inv6, 6.0 * (double)g);
+        if constexpr (RULE == FOUR6) k4 = select_sf_exact<SF>(bitsf(amax), inv4, 4.0 * (double)g);
       }
       if (p.prevent_zero && k6 == 0) k6 = 1;
-      const float s6 = e4m3_f32(k6);
-      uint2 packed = encode_nv16<LPB>(x, k6, s6, g, finite);
+      const float s6 = sf_f32<SF>(k6);
+      uint2 packed = encode_nv16<LPB, SF>(x, k6, s6, g, finite);
       int sbyte = k6;
       if constexpr (RULE == FOUR6) {
         if (p.prevent_zero && k4 == 0) k4 = 1;
-        const float s4 = e4m3_f32(k4);
-        const uint2 pk4 = encode_nv16<LPB>(x, k4, s4, g, finite);
+        const float s4 = sf_f32<SF>(k4);
+        const uint2 pk4 = encode_nv16<LPB, SF>(x, k4, s4, g, finite);
         // a -0 code (0x8) decodes to -0 and gives the same error as +0
         const float e6 = group_sum<LPB>(lane_sse16(x, packed, s6, g));
         const float e4 = group_sum<LPB>(lane_sse16(x, pk4, s4, g));
@@ -1001,7 +1026,81 @@ __device__ __forceinline__ void load_run32(const QuantParams& p, int64_t r, int6
   }
 }
 
-template <bool BF16, bool CHAN, bool HAD>
+// MXFP4 codes of 32 elements at shared exponent E >= -126 (a normal FP32
+// scale, which the convert divides by exactly, rounding to nearest even)
+__device__ __forceinline__ void mx_encode32(const float* x, int E, uint32_t (&pk)[4]) {
+  const float sc = bitsf((uint32_t)(E + 127) << 23);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = 0;
+    static_for<0, 4>([&](auto ic) {
+      constexpr int b = decltype(ic)::value;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * q + 2 * b], x[8 * q + 2 * b + 1], sc, b);
+    });
+    pk[q] = clear_neg_zero(w);
+  }
+}
+
+// block error of 32 elements with codes pk at exponent E: value * 2^E is
+// exact, e = x - value * 2^E in one rounding (the oracle's fma with g = 1),
+// squares, the balanced tree
+__device__ __forceinline__ float mx_sse32(const float* x, const uint32_t (&pk)[4], float sc) {
+  float part[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float pp[8];
+    static_for<0, 4>([&](auto ic) {
+      constexpr int b = decltype(ic)::value;
+      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[q], 1.0f, b);
+      const float e0 = x[8 * q + 2 * b] - v2[0] * sc, e1 = x[8 * q + 2 * b + 1] - v2[1] * sc;
+      pp[2 * b] = e0 * e0;
+      pp[2 * b + 1] = e1 * e1;
+    });
+    part[q] = tree_sum<8>(pp);
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// The same for any E in [-127, 127] (a block near the bottom of the FP32
+// range): the exact threshold encode, and value * 2^E formed by ldexpf
+// (exact, subnormal results included).  Out of line: rare.
+struct MxCand {
+  uint32_t pk[4];
+  float sse;
+};
+__device__ __attribute__((noinline)) MxCand mx_candidate_exact(float __attribute__((ext_vector_type(32))) xv, int E) {
+  MxCand out;
+  uint32_t* pk = out.pk;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = xv[i];
+  typedef float f8v __attribute__((ext_vector_type(8)));
+  float part[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f8v w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = x[8 * q + i];
+    pk[q] = encode_mx_thresholds<8>(w, E);
+    float pp[8];
+    static_for<0, 4>([&](auto ic) {
+      constexpr int b = decltype(ic)::value;
+      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[q], 1.0f, b);
+      const float e0 = x[8 * q + 2 * b] - ldexpf(v2[0], E), e1 = x[8 * q + 2 * b + 1] - ldexpf(v2[1], E);
+      pp[2 * b] = e0 * e0;
+      pp[2 * b + 1] = e1 * e1;
+    });
+    part[q] = tree_sum<8>(pp);
+  }
+  out.sse = (part[0] + part[1]) + (part[2] + part[3]);
+  return out;
+}
+
+// HS: block-Hadamard size (0, 16, 32).  RULE: ABSMAX (the standard
+// exponent), or EXPSEARCH: the standard exponent E and the offsets E + 1 and
+// E - 1 (MACaQ section 1's candidates) compared by plain block error, in that
+// order, the strictly smallest kept.
+template <bool BF16, bool CHAN, int HS, int RULE>
 __global__ __launch_bounds__(kThreads) void mx32_kernel(QuantParams p) {
   constexpr int L = 32, W = BF16 ? 16 : 32;
   const int64_t rpr = p.cols / L;
@@ -1047,23 +1146,7 @@ __global__ __launch_bounds__(kThreads) void mx32_kernel(QuantParams p) {
 #pragma unroll
         for (int i = 0; i < L; ++i) x[i] = x[i] * tc[i];
       }
-      if constexpr (HAD) {
-        // natural-order FWHT of the 32 values, then the orthonormal factor
-#pragma unroll
-        for (int h = 1; h < L; h *= 2) {
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            if ((i & h) == 0) {
-              const float a = x[i], b = x[i + h];
-              x[i] = a + b;
-              x[i + h] = a - b;
-            }
-          }
-        }
-        const float c = bitsf(0x3E3504F3u);  // RN32(2^-2.5)
-#pragma unroll
-        for (int i = 0; i < L; ++i) x[i] = x[i] * c;
-      }
+      if constexpr (HS > 0) block_hadamard<L, HS>(x);
       uint32_t amax = 0;
 #pragma unroll
       for (int i = 0; i < L; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
@@ -1075,19 +1158,49 @@ __global__ __launch_bounds__(kThreads) void mx32_kernel(QuantParams p) {
         const int fl = ex ? ex - 127 : (31 - __clz((int)amax)) - 149;
         E = max(-127, fl - 2);
       }
+      const bool finite = amax < 0x7F800000u;
       uint32_t pk[4];
-      if (E >= -126 && amax < 0x7F800000u) {
-        // the convert divides by 2^E exactly and rounds to nearest even
-        const float sc = bitsf((uint32_t)(E + 127) << 23);
+      if constexpr (RULE == EXPSEARCH) {
+        // the lowest candidate E - 1 must be a normal scale for the fast path;
+        // E + 1 <= 126 always holds for a finite block
+        int Eb = E;
+        if (E - 1 >= -126 && finite) {
+          mx_encode32(x, E, pk);
+          float best = mx_sse32(x, pk, bitsf((uint32_t)(E + 127) << 23));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t w = 0;
-          static_for<0, 4>([&](auto ic) {
-            constexpr int b = decltype(ic)::value;
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * q + 2 * b], x[8 * q + 2 * b + 1], sc, b);
-          });
-          pk[q] = clear_neg_zero(w);
+          for (int c = 0; c < 2; ++c) {
+            const int Ec = c == 0 ? E + 1 : E - 1;
+            uint32_t pc[4];
+            mx_encode32(x, Ec, pc);
+            const float e = mx_sse32(x, pc, bitsf((uint32_t)(Ec + 127) << 23));
+            if (e < best) {
+              best = e;
+              Eb = Ec;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) pk[q] = pc[q];
+            }
+          }
+        } else {
+          typedef float f32v __attribute__((ext_vector_type(32)));
+          f32v xv;
+#pragma unroll
+          for (int i = 0; i < L; ++i) xv[i] = x[i];
+          MxCand best = mx_candidate_exact(xv, E);
+          for (int c = 0; c < 2; ++c) {
+            const int Ec = c == 0 ? E + 1 : E - 1;
+            if (Ec < -127 || Ec > 127) continue;
+            const MxCand cand = mx_candidate_exact(xv, Ec);
+            if (cand.sse < best.sse) {
+              best = cand;
+              Eb = Ec;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pk[q] = best.pk[q];
         }
+        E = Eb;
+      } else if (E >= -126 && finite) {
+        mx_encode32(x, E, pk);
       } else {
         typedef float f8v __attribute__((ext_vector_type(8)));
 #pragma unroll
@@ -1143,7 +1256,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(QuantParams p) {
   constexpr int L = 8;
   constexpr int U = CONTIG ? 2 : 1;
   const bool chan = p.chan_scale != nullptr;
-  const bool had = p.hadamard == 32;
+  const int had = p.hadamard;
   const int64_t cpr = p.cols / L;
   const int64_t total = p.rows * cpr;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -1224,6 +1337,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantParams p) {
     const uint8_t sb = p.scales[r * (p.cols / B) + j0 / B];
     float s, v = 0.f;
     if constexpr (FMT == MXFP4) s = ldexpf(1.0f, (int)sb - 127);
+    else if constexpr (FMT == UE5M3) s = ue5m3_f32(sb);
     else if constexpr (FMT == RAZER_W) { s = (float)sf_val<1>(sb & 0x3F); v = p.special[sb >> 6]; }
     else { s = (float)sf_val<0>(sb & 0x7F); v = (sb & 0x80) ? -5.0f : 5.0f; }
     float out[L];
@@ -1329,12 +1443,12 @@ hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
   }
   // the brute-force search is compute-bound: one addressing variant suffices
   const bool contig = RULE != BRUTE && p.ld == p.cols && p.chan_scale == nullptr;
-  if constexpr (FMT == NVFP4 && RULE != BRUTE && B >= 16) {
+  if constexpr ((FMT == NVFP4 || FMT == UE5M3) && RULE != BRUTE && B >= 16) {
     if (contig && p.fused_denom == 0.0f) {
       // two runs per thread and iteration: at least one whole iteration each
       const int g16 = grid_for((p.rows * (p.cols / 16) + 1) / 2);
-      if (bf16) hipLaunchKernelGGL((nv16_kernel<B, RULE, true>), dim3(g16), dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((nv16_kernel<B, RULE, false>), dim3(g16), dim3(kThreads), 0, s, p);
+      if (bf16) hipLaunchKernelGGL((nv16_kernel<FMT, B, RULE, true>), dim3(g16), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((nv16_kernel<FMT, B, RULE, false>), dim3(g16), dim3(kThreads), 0, s, p);
       return hipGetLastError();
     }
   }
@@ -1356,6 +1470,21 @@ hipError_t launch_q2(int block, bool bf16, const QuantParams& p, hipStream_t s) 
     case 16: return launch_q3<FMT, 16, RULE>(bf16, p, s);
     default: return launch_q3<FMT, 32, RULE>(bf16, p, s);
   }
+}
+
+template <int RULE, bool BF16, bool CHAN>
+hipError_t launch_mx_hs(const QuantParams& q, int grid, hipStream_t s) {
+  if (q.hadamard == 32) hipLaunchKernelGGL((mx32_kernel<BF16, CHAN, 32, RULE>), dim3(grid), dim3(kThreads), 0, s, q);
+  else if (q.hadamard == 16) hipLaunchKernelGGL((mx32_kernel<BF16, CHAN, 16, RULE>), dim3(grid), dim3(kThreads), 0, s, q);
+  else hipLaunchKernelGGL((mx32_kernel<BF16, CHAN, 0, RULE>), dim3(grid), dim3(kThreads), 0, s, q);
+  return hipGetLastError();
+}
+
+template <int RULE>
+hipError_t launch_mx(bool bf16, const QuantParams& q, int grid, hipStream_t s) {
+  const bool chan = q.chan_scale != nullptr;
+  if (bf16) return chan ? launch_mx_hs<RULE, true, true>(q, grid, s) : launch_mx_hs<RULE, true, false>(q, grid, s);
+  return chan ? launch_mx_hs<RULE, false, true>(q, grid, s) : launch_mx_hs<RULE, false, false>(q, grid, s);
 }
 
 }  // namespace
@@ -1395,20 +1524,14 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
     case MXFP4: {
       const int64_t rpr = q.cols / 32;
       const int grid = mx32_grid(q.rows, rpr);
-      const bool chan = q.chan_scale != nullptr, had = q.hadamard == 32;
-#define FP4Q_MX(BF, CH, HD) hipLaunchKernelGGL((mx32_kernel<BF, CH, HD>), dim3(grid), dim3(kThreads), 0, s, q)
-      if (bf16) {
-        if (chan) { if (had) FP4Q_MX(true, true, true); else FP4Q_MX(true, true, false); }
-        else { if (had) FP4Q_MX(true, false, true); else FP4Q_MX(true, false, false); }
-      } else {
-        if (chan) { if (had) FP4Q_MX(false, true, true); else FP4Q_MX(false, true, false); }
-        else { if (had) FP4Q_MX(false, false, true); else FP4Q_MX(false, false, false); }
-      }
-#undef FP4Q_MX
-      return hipGetLastError();
+      return rule == EXPSEARCH ? launch_mx<EXPSEARCH>(bf16, q, grid, s) : launch_mx<ABSMAX>(bf16, q, grid, s);
     }
     case RAZER_A: return launch_q2<RAZER_A, ABSMAX>(block, bf16, q, s);
     case RAZER_W: return launch_q2<RAZER_W, ABSMAX>(block, bf16, q, s);
+    case UE5M3:
+      if (rule == FOUR6) return launch_q2<UE5M3, FOUR6>(block, bf16, q, s);
+      if (rule == BRUTE) return launch_q2<UE5M3, BRUTE>(block, bf16, q, s);
+      return launch_q2<UE5M3, ABSMAX>(block, bf16, q, s);
     default:
       if (rule == FOUR6) return launch_q2<NVFP4, FOUR6>(block, bf16, q, s);
       if (rule == BRUTE) return launch_q2<NVFP4, BRUTE>(block, bf16, q, s);
@@ -1430,6 +1553,10 @@ hipError_t launch_dequantize(int fmt, int block, const DequantParams& p, hipStre
     case RAZER_A:
       if (block == 4) FP4Q_DQ(RAZER_A, 4); else if (block == 8) FP4Q_DQ(RAZER_A, 8);
       else if (block == 16) FP4Q_DQ(RAZER_A, 16); else FP4Q_DQ(RAZER_A, 32);
+      break;
+    case UE5M3:
+      if (block == 4) FP4Q_DQ(UE5M3, 4); else if (block == 8) FP4Q_DQ(UE5M3, 8);
+      else if (block == 16) FP4Q_DQ(UE5M3, 16); else FP4Q_DQ(UE5M3, 32);
       break;
     default:
       if (block == 4) FP4Q_DQ(RAZER_W, 4); else if (block == 8) FP4Q_DQ(RAZER_W, 8);

@@ -15,6 +15,12 @@
  *   RAZER_W  E2M1 elements with a 6-bit E3M3 scale; the top two bits of the
  *            scale byte pick one of four special values; code 0x8 decodes to
  *            it.  RaZeR summary, sections 2.1-2.2.
+ *   UE5M3    E2M1 elements with an unsigned 8-bit UE5M3 scale per block of 4,
+ *            8, 16 or 32 (5 exponent bits, bias 15, 3 mantissa bits,
+ *            subnormals, no special codes: 0 .. 122880); the wide-exponent
+ *            scale "Finer is Better" compares with E4M3 + 4-over-6 +
+ *            hierarchical scaling (findings, claims).  Global mode NONE or
+ *            GIVEN; quantize and dequantize only.
  *
  * Layout (every buffer row-major, blocks run along the last, contiguous
  * dimension):
@@ -26,6 +32,7 @@
  *             MXFP4    E8M0 code (2^(code-127))
  *             RAZER_A  bit 7 = pick (0: +5, 1: -5), bits 6:0 = E4M3 code
  *             RAZER_W  bits 7:6 = index into special[4], bits 5:0 = E3M3 code
+ *             UE5M3    UE5M3 code
  *   global  one FP32 on the device; an element decodes to value * scale * g.
  *
  * Ownership: the caller allocates and owns every buffer it passes.  The only
@@ -67,7 +74,8 @@ typedef enum {
   FP4Q_NVFP4 = 0,
   FP4Q_MXFP4 = 1,
   FP4Q_NVFP4_RAZER_A = 2,
-  FP4Q_NVFP4_RAZER_W = 3
+  FP4Q_NVFP4_RAZER_W = 3,
+  FP4Q_UE5M3 = 4          /* quantize / dequantize only                        */
 } fp4q_format;
 
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
@@ -77,7 +85,9 @@ typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
 enum {
   FP4Q_RULE_ABSMAX = 0,        /* block max maps to 6, nearest E4M3 scale          */
   FP4Q_RULE_4OVER6 = 1,        /* max maps to 4 or 6, lower block error kept       */
-  FP4Q_RULE_BRUTE = 2,         /* all 126 positive E4M3 scales, lowest error kept  */
+  FP4Q_RULE_BRUTE = 2,         /* every positive scale, lowest error kept         */
+  FP4Q_RULE_EXPSEARCH = 3,     /* MXFP4: shared exponent E, E+1 or E-1, lowest
+                                  block error kept (ties: that order)             */
   FP4Q_FLAG_PREVENT_ZERO = 0x100 /* a zero scale is raised to the smallest positive */
 };
 
@@ -93,14 +103,16 @@ typedef struct {
   uint32_t struct_size;
   fp4q_format format;
   int32_t block;               /* NVFP4 family: 4, 8, 16 or 32; MXFP4: 32        */
-  uint32_t rule;               /* rule | flags; RaZeR formats and MXFP4 take
-                                  ABSMAX (RaZeR may add PREVENT_ZERO)            */
-  fp4q_global_mode global_mode;/* MXFP4: must be NONE                            */
+  uint32_t rule;               /* rule | flags.  NVFP4, UE5M3: ABSMAX, 4OVER6,
+                                  BRUTE (+ PREVENT_ZERO); MXFP4: ABSMAX or
+                                  EXPSEARCH; RaZeR: ABSMAX (+ PREVENT_ZERO)      */
+  fp4q_global_mode global_mode;/* MXFP4: NONE; UE5M3: NONE or GIVEN              */
   const float* chan_scale;     /* device, `cols` floats, or NULL: x_j *= t_j
                                   before quantization (MACaQ online scaling)     */
-  int32_t hadamard;            /* 0, or 32: size-32 block-Hadamard after the
-                                  channel scale (MACaQ micro-rotation);
-                                  needs cols % 32 == 0                           */
+  int32_t hadamard;            /* 0, 32 or 16: orthonormal block-Hadamard of
+                                  that size after the channel scale (MACaQ
+                                  micro-rotation; 16 matches the NVFP4 block);
+                                  needs cols % hadamard == 0                     */
   float special[4];            /* RAZER_W: the four special values; each a
                                   multiple of 0.5 with 0 < |v| <= 7.5 that is
                                   not an E2M1 magnitude.  Ignored otherwise.     */
@@ -108,8 +120,8 @@ typedef struct {
 
 /*
  * Quantize a rows x cols tensor x (fp32 or bf16, row pitch ld_x elements).
- * Steps: widen to fp32; x_j *= chan_scale[j] (if given); size-32
- * block-Hadamard (if hadamard == 32); global scale per global_mode; per-block
+ * Steps: widen to fp32; x_j *= chan_scale[j] (if given); block-Hadamard
+ * (if hadamard is 16 or 32); global scale per global_mode; per-block
  * scale by the rule; E2M1 encode (RaZeR: with the special value); pack.
  * Pages: scale rules -- "Finer is Better", Method 2; RaZeR picks -- RaZeR
  * summary 2.2; transforms -- MACaQ review, sections 1 and 3; MXFP4 -- MACaQ
@@ -119,7 +131,7 @@ typedef struct {
  *   scales  device, rows*(cols/block) bytes, written
  *   global  device FP32: read (GIVEN), written (AUTO) or unused (NONE, may be NULL)
  * Errors: NULL desc/x/codes/scales (or global with AUTO/GIVEN) -> ERR_NULL;
- * rows < 0, cols <= 0, cols % block, ld_x < cols, hadamard with cols % 32
+ * rows < 0, cols <= 0, cols % block, ld_x < cols, cols % hadamard
  * -> ERR_SHAPE; misalignment -> ERR_ALIGN; bad format -> ERR_FORMAT; bad rule,
  * flag, block, mode, struct_size, hadamard or special value -> ERR_ARG.
  * rows == 0 is valid and enqueues nothing (AUTO then writes nothing).
@@ -164,7 +176,8 @@ fp4q_status fp4q_dequantize(const fp4q_quant_desc* desc, const uint8_t* codes,
  *   c         device, M x N (pitch ldc elements), 16-byte aligned
  * Errors: NULL pointer -> ERR_NULL; M, N < 0, K <= 0, K % block, K > 2^24
  * (operand offsets within a 256-row panel are 32-bit), more than 2^31 - 1
- * tiles of 256 x 256, or ldc < N -> ERR_SHAPE; a mixed MXFP4/NVFP4 pair or fa == RAZER_W -> ERR_FORMAT;
+ * tiles of 256 x 256, or ldc < N -> ERR_SHAPE; a mixed MXFP4/NVFP4 pair,
+ * fa == RAZER_W, or a UE5M3 operand -> ERR_FORMAT;
  * bad special value
  * -> ERR_ARG; misalignment -> ERR_ALIGN.  M == 0 or N == 0 enqueues nothing.
  */

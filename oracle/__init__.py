@@ -22,14 +22,14 @@ _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
 # formats, rules, global modes (the oracle's own numbering)
-NVFP4, MXFP4, RAZER_A, RAZER_W = 0, 1, 2, 3
-ABSMAX, FOUR_OVER_SIX, BRUTE = 0, 1, 2
+NVFP4, MXFP4, RAZER_A, RAZER_W, UE5M3 = 0, 1, 2, 3, 4
+ABSMAX, FOUR_OVER_SIX, BRUTE, EXPSEARCH = 0, 1, 2, 3
 PREVENT_ZERO = 0x100
 G_NONE, G_AUTO, G_GIVEN = 0, 1, 2
-SF_E4M3, SF_E3M3 = 0, 1
+SF_E4M3, SF_E3M3, SF_UE5M3 = 0, 1, 2
 F32, BF16 = 0, 1
 
-FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4, "razer_a": RAZER_A, "razer_w": RAZER_W}
+FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4, "razer_a": RAZER_A, "razer_w": RAZER_W, "ue5m3": UE5M3}
 
 
 def build(force: bool = False) -> str:
@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         d, i, f, l, vp = ctypes.c_double, ctypes.c_int, ctypes.c_float, ctypes.c_long, ctypes.c_void_p
         sig = {
             "or_e2m1_value": (d, [i]), "or_e4m3_value": (d, [i]),
-            "or_e3m3_value": (d, [i]), "or_e8m0_value": (d, [i]),
+            "or_e3m3_value": (d, [i]), "or_e8m0_value": (d, [i]), "or_ue5m3_value": (d, [i]),
             "or_round_scale": (i, [i, d, d, d]),
             "or_rtn": (i, [f, d, d]),
             "or_rtn_special": (i, [f, d, d, d]),
@@ -107,6 +107,7 @@ def e2m1_value(c: int) -> float: return lib().or_e2m1_value(c)
 def e4m3_value(k: int) -> float: return lib().or_e4m3_value(k)
 def e3m3_value(k: int) -> float: return lib().or_e3m3_value(k)
 def e8m0_value(k: int) -> float: return lib().or_e8m0_value(k)
+def ue5m3_value(k: int) -> float: return lib().or_ue5m3_value(k)
 def round_scale(sf: int, a: float, T: float, g: float) -> int: return lib().or_round_scale(sf, a, T, g)
 def rtn(x: float, s: float, g: float) -> int: return lib().or_rtn(x, s, g)
 def rtn_special(x: float, s: float, g: float, v: float) -> int: return lib().or_rtn_special(x, s, g, v)

@@ -47,8 +47,23 @@ double or_e3m3_value(int k) {
 /* E8M0: a bare power of two, the MXFP4 shared scale of [MACaQ] section 1. */
 double or_e8m0_value(int k) { return ldexp(1.0, k - 127); }
 
-static double sf_value(int sf, int k) { return sf == OR_SF_E4M3 ? or_e4m3_value(k) : or_e3m3_value(k); }
-static int sf_max_code(int sf) { return sf == OR_SF_E4M3 ? 126 : 63; }
+/* UE5M3: the unsigned wide-exponent block scale that [Finer] findings and
+ * claims compare with E4M3 + 4-over-6 + hierarchical scaling.  The page gives
+ * only the name; read here as 5 exponent bits (bias 15, the half-precision
+ * bias) and 3 mantissa bits, subnormals, no sign and no special codes: 256
+ * values from 0 to 1.875 * 2^16 = 122880, smallest positive 2^-17. */
+double or_ue5m3_value(int k) {
+  int e = k >> 3, m = k & 7;
+  if (e == 0) return ldexp((double)m, -17);
+  return ldexp((double)(8 + m), e - 18);
+}
+
+static double sf_value(int sf, int k) {
+  if (sf == OR_SF_E4M3) return or_e4m3_value(k);
+  if (sf == OR_SF_E3M3) return or_e3m3_value(k);
+  return or_ue5m3_value(k);
+}
+static int sf_max_code(int sf) { return sf == OR_SF_E4M3 ? 126 : sf == OR_SF_E3M3 ? 63 : 255; }
 
 /* ------------------------------------------------------------------------- */
 /* Rounding primitives                                                       */
@@ -173,18 +188,41 @@ static uint8_t quant_block(int format, int B, int rule, const float* special4,
     if (E < -127) E = -127;
     if (E > 127) E = 127;
     encode_plain(x, B, ldexp(1.0, E), 1.0, codes);
-    return (uint8_t)(E + 127);
+    if (r != OR_EXPSEARCH) return (uint8_t)(E + 127);
+    /* [MACaQ] section 1 compares the standard exponent with offsets +1 and
+     * -1 by a Hessian-weighted error; with a plain block error (unit
+     * Hessian) that is the search below.  Candidates in the order E, E+1,
+     * E-1 (those inside the E8M0 range); the strictly smallest block error
+     * wins, a tie keeps the earlier candidate. */
+    float best = or_block_sse(x, codes, B, ldexp(1.0, E), 1.0f, 0, 0.0);
+    int bestE = E;
+    const int off[2] = {1, -1};
+    int tmp[32];
+    for (int t = 0; t < 2; ++t) {
+      int Ec = E + off[t];
+      if (Ec < -127 || Ec > 127) continue;
+      encode_plain(x, B, ldexp(1.0, Ec), 1.0, tmp);
+      float e = or_block_sse(x, tmp, B, ldexp(1.0, Ec), 1.0f, 0, 0.0);
+      if (e < best) {
+        best = e;
+        bestE = Ec;
+        memcpy(codes, tmp, sizeof(int) * B);
+      }
+    }
+    return (uint8_t)(bestE + 127);
   }
 
-  if (format == OR_NVFP4) {
+  if (format == OR_NVFP4 || format == OR_UE5M3) {
+    const int sf = format == OR_NVFP4 ? OR_SF_E4M3 : OR_SF_UE5M3;
     if (r == OR_BRUTE) {
-      /* [Finer] Method 2 "brute-force": every positive finite E4M3 scale is
-       * tried; the strictly smallest error wins, a tie keeps the smaller code. */
+      /* [Finer] Method 2 "brute-force": every positive finite scale of the
+       * format is tried; the strictly smallest error wins, a tie keeps the
+       * smaller code. */
       int best_k = 1;
       float best = 0.0f;
       int tmp[32];
-      for (int k = 1; k <= 126; ++k) {
-        double s = or_e4m3_value(k);
+      for (int k = 1; k <= sf_max_code(sf); ++k) {
+        double s = sf_value(sf, k);
         encode_plain(x, B, s, gd, tmp);
         float e = or_block_sse(x, tmp, B, s, g, 0, 0.0);
         if (k == 1 || e < best) {
@@ -196,21 +234,21 @@ static uint8_t quant_block(int format, int B, int rule, const float* special4,
       return (uint8_t)best_k;
     }
     /* [Finer] Method 2 "abs-max": the block max maps to 6.0 */
-    int k6 = or_round_scale(OR_SF_E4M3, a, 6.0, gd);
+    int k6 = or_round_scale(sf, a, 6.0, gd);
     /* [Finer] Method 2 "prevent-zero": a zero scale is raised to the smallest
-     * positive representable E4M3 value (2^-9) */
+     * positive representable scale (2^-9 for E4M3, 2^-17 for UE5M3) */
     if (pz && k6 == 0) k6 = 1;
-    encode_plain(x, B, or_e4m3_value(k6), gd, codes);
+    encode_plain(x, B, sf_value(sf, k6), gd, codes);
     if (r == OR_ABSMAX) return (uint8_t)k6;
     /* [Finer] Method 2 "4-over-6": the block max maps to 4.0 or to 6.0,
      * whichever block error is lower; both candidates are quantized.  A tie
      * keeps 6. */
-    int k4 = or_round_scale(OR_SF_E4M3, a, 4.0, gd);
+    int k4 = or_round_scale(sf, a, 4.0, gd);
     if (pz && k4 == 0) k4 = 1;
     int c4[32];
-    encode_plain(x, B, or_e4m3_value(k4), gd, c4);
-    float e6 = or_block_sse(x, codes, B, or_e4m3_value(k6), g, 0, 0.0);
-    float e4 = or_block_sse(x, c4, B, or_e4m3_value(k4), g, 0, 0.0);
+    encode_plain(x, B, sf_value(sf, k4), gd, c4);
+    float e6 = or_block_sse(x, codes, B, sf_value(sf, k6), g, 0, 0.0);
+    float e4 = or_block_sse(x, c4, B, sf_value(sf, k4), g, 0, 0.0);
     if (e4 < e6) {
       memcpy(codes, c4, sizeof(int) * B);
       return (uint8_t)k4;
@@ -282,11 +320,11 @@ static float load_elem(const void* x, int dt, long idx) {
   return f;
 }
 
-/* Sylvester-ordered fast Walsh-Hadamard transform of 32 values in binary32:
- * for h = 1, 2, 4, 8, 16 the pairs (j, j+h) become (u+w, u-w). */
-static void fwht32(float* y) {
-  for (int h = 1; h < 32; h *= 2)
-    for (int i = 0; i < 32; i += 2 * h)
+/* Sylvester-ordered fast Walsh-Hadamard transform of n (16 or 32) values in
+ * binary32: for h = 1, 2, 4, ... < n the pairs (j, j+h) become (u+w, u-w). */
+static void fwht(float* y, int n) {
+  for (int h = 1; h < n; h *= 2)
+    for (int i = 0; i < n; i += 2 * h)
       for (int j = i; j < i + h; ++j) {
         float u = y[j], w = y[j + h];
         y[j] = u + w;
@@ -297,22 +335,25 @@ static void fwht32(float* y) {
 /* [MACaQ] sections 1 and 3: the online per-channel scale D (x_j * t_j) and
  * then the size-32 block-Hadamard B, normalised to be orthonormal by
  * c = RN32(2^-2.5); the weight side absorbs W D^-1 B, i.e. the same call with
- * t_j replaced by 1/t_j. */
+ * t_j replaced by 1/t_j.  hadamard = 16 is the NVFP4-block-sized variant
+ * ("Finer is Better" claims compare scale formats; the MACaQ page sizes the
+ * rotation to the block): groups of 16, normalised by exactly 1/4. */
 void or_transform(const void* x, int xdtype, long rows, long cols, long ld,
                   const float* t, int hadamard, float* out) {
   uint32_t cbits = 0x3E3504F3u;
   float c;
   memcpy(&c, &cbits, 4);
+  if (hadamard == 16) c = 0.25f;
   for (long r = 0; r < rows; ++r) {
     float* y = out + r * cols;
     for (long j = 0; j < cols; ++j) {
       float v = load_elem(x, xdtype, r * ld + j);
       y[j] = t ? v * t[j] : v;
     }
-    if (hadamard == 32)
-      for (long j0 = 0; j0 < cols; j0 += 32) {
-        fwht32(y + j0);
-        for (int i = 0; i < 32; ++i) y[j0 + i] = y[j0 + i] * c;
+    if (hadamard == 16 || hadamard == 32)
+      for (long j0 = 0; j0 < cols; j0 += hadamard) {
+        fwht(y + j0, hadamard);
+        for (int i = 0; i < hadamard; ++i) y[j0 + i] = y[j0 + i] * c;
       }
   }
 }
@@ -332,17 +373,17 @@ float or_auto_global(const float* xt, long rows, long cols, int format) {
 }
 
 static int check_format(int format, int block, int rule, int hadamard, long cols) {
-  if (format < OR_NVFP4 || format > OR_RAZER_W) return -1;
+  if (format < OR_NVFP4 || format > OR_UE5M3) return -1;
   if (format == OR_MXFP4) {
-    if (block != 32 || rule != OR_ABSMAX) return -1;
+    if (block != 32 || (rule != OR_ABSMAX && rule != OR_EXPSEARCH)) return -1;
   } else {
     if (block != 4 && block != 8 && block != 16 && block != 32) return -1;
     int r = rule & 0xff;
     if ((rule & ~0x1ff) != 0 || r > OR_BRUTE) return -1;
     if ((format == OR_RAZER_A || format == OR_RAZER_W) && r != OR_ABSMAX) return -1;
   }
-  if (hadamard != 0 && hadamard != 32) return -1;
-  if (cols <= 0 || cols % block != 0 || (hadamard && cols % 32 != 0)) return -1;
+  if (hadamard != 0 && hadamard != 16 && hadamard != 32) return -1;
+  if (cols <= 0 || cols % block != 0 || (hadamard && cols % hadamard != 0)) return -1;
   return 0;
 }
 
@@ -372,6 +413,8 @@ int or_quantize(int format, int block, int rule, int gmode, const float* chan_sc
                 float* g_inout) {
   if (check_format(format, block, rule, hadamard, cols)) return -1;
   if (format == OR_MXFP4 && gmode != OR_G_NONE) return -1;
+  /* UE5M3's range needs no hierarchical scale ([Finer] claims): no AUTO */
+  if (format == OR_UE5M3 && gmode == OR_G_AUTO) return -1;
   float* xt = (float*)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1) * (size_t)cols);
   if (!xt) return -2;
   or_transform(x, xdtype, rows, cols, ld, chan_scale, hadamard, xt);
@@ -390,6 +433,7 @@ static double decode_elem(int format, const float* special4, int c, uint8_t sb) 
   switch (format) {
     case OR_NVFP4: return or_e2m1_value(c) * or_e4m3_value(sb & 0x7f);
     case OR_MXFP4: return or_e2m1_value(c) * or_e8m0_value(sb);
+    case OR_UE5M3: return or_e2m1_value(c) * or_ue5m3_value(sb);
     case OR_RAZER_A: {
       double s = or_e4m3_value(sb & 0x7f);
       if (c == 8) return ((sb & 0x80) ? -5.0 : 5.0) * s;
@@ -405,7 +449,7 @@ static double decode_elem(int format, const float* special4, int c, uint8_t sb) 
 
 int or_decode_row(int format, int block, const float* special4, const uint8_t* codes_row,
                   const uint8_t* scales_row, long cols, double* out) {
-  if (format < OR_NVFP4 || format > OR_RAZER_W || block <= 0 || cols % block) return -1;
+  if (format < OR_NVFP4 || format > OR_UE5M3 || block <= 0 || cols % block) return -1;
   for (long j = 0; j < cols; ++j) {
     int c = (codes_row[j / 2] >> (4 * (j & 1))) & 15;
     out[j] = decode_elem(format, special4, c, scales_row[j / block]);
@@ -415,7 +459,7 @@ int or_decode_row(int format, int block, const float* special4, const uint8_t* c
 
 int or_dequantize(int format, int block, const float* special4, const uint8_t* codes,
                   const uint8_t* scales, float g, long rows, long cols, float* out) {
-  if (format < OR_NVFP4 || format > OR_RAZER_W || block <= 0 || cols % block) return -1;
+  if (format < OR_NVFP4 || format > OR_UE5M3 || block <= 0 || cols % block) return -1;
   double* row = (double*)malloc(sizeof(double) * (size_t)cols);
   if (!row) return -2;
   for (long r = 0; r < rows; ++r) {

@@ -37,11 +37,13 @@ extern "C" {
 #define OR_MXFP4   1   /* E2M1 + E8M0 per 32-element block                */
 #define OR_RAZER_A 2   /* NVFP4, E4M3 sign bit = pick of +5 / -5          */
 #define OR_RAZER_W 3   /* E3M3 scale + 2-bit pick among 4 special values   */
+#define OR_UE5M3   4   /* E2M1 + UE5M3 (unsigned, 5-bit exponent) per block */
 
 /* scale rules (low byte) and flags */
 #define OR_ABSMAX       0
 #define OR_4OVER6       1
 #define OR_BRUTE        2
+#define OR_EXPSEARCH    3   /* MXFP4: shared exponent E_std, E_std+1, E_std-1 by block error */
 #define OR_PREVENT_ZERO 0x100
 
 /* global scale modes */
@@ -56,12 +58,14 @@ extern "C" {
 /* scale formats for or_round_scale */
 #define OR_SF_E4M3 0
 #define OR_SF_E3M3 1
+#define OR_SF_UE5M3 2
 
 /* -- number formats --------------------------------------------------------- */
 double or_e2m1_value(int code);   /* signed value of a 4-bit E2M1 code          */
 double or_e4m3_value(int k);      /* k in 0..126 (OCP E4M3, sign bit clear)     */
 double or_e3m3_value(int k);      /* k in 0..63  (6-bit, bias 3)                */
 double or_e8m0_value(int k);      /* k in 0..254                                */
+double or_ue5m3_value(int k);     /* k in 0..255 (unsigned, bias 15)            */
 
 /* -- rounding primitives ------------------------------------------------------ */
 /* nearest code of scale format sf to a/(T*g); ties to the even code; saturates */
@@ -78,8 +82,9 @@ float or_block_sse(const float* x, const int* codes, int n, double s, float g,
                    int has_special, double v);
 
 /* -- whole-tensor operations -------------------------------------------------- */
-/* widen (bf16 -> fp32), channel scale x_j*t_j, then size-32 block-Hadamard.
- * t may be NULL; hadamard is 0 or 32.  out is rows x cols fp32, contiguous. */
+/* widen (bf16 -> fp32), channel scale x_j*t_j, then the block-Hadamard of
+ * size 16 or 32 (orthonormal).  t may be NULL; hadamard is 0, 16 or 32.  out
+ * is rows x cols fp32, contiguous. */
 void or_transform(const void* x, int xdtype, long rows, long cols, long ld,
                   const float* t, int hadamard, float* out);
 

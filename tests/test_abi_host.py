@@ -126,7 +126,10 @@ res = {
  "q_bad_rule": q(d=desc(rule=3)), "q_bad_flag": q(d=desc(rule=0x200)),
  "q_razer_rule": q(d=desc(format=2, rule=1)), "q_mx_rule": q(d=desc(format=1, block=32, rule=1)),
  "q_mx_pz": q(d=desc(format=1, block=32, rule=0x100)), "q_mx_global": q(d=desc(format=1, block=32, global_mode=1)),
- "q_bad_mode": q(d=desc(global_mode=3)), "q_bad_had": q(d=desc(hadamard=16)),
+ "q_bad_mode": q(d=desc(global_mode=3)), "q_bad_had": q(d=desc(hadamard=8)),
+ "q_had16_cols": q(d=desc(hadamard=16, block=4), cols=40, ld=40),
+ "q_ue5m3_auto": q(d=desc(format=4, global_mode=1)), "q_ue5m3_rule": q(d=desc(format=4, rule=3)),
+ "q_nv_expsearch": q(d=desc(rule=3)), "q_bad_format5": q(d=desc(format=5)),
  "q_bad_dtype": q(xt=2),
  "q_special_grid": q(d=desc(format=3, special=(5.0, -5.0, 2.5, 4.0))),
  "q_special_half": q(d=desc(format=3, special=(5.0, -5.0, 2.25, -2.5))),
@@ -140,7 +143,7 @@ res = {
  # gemm
  "g_null_a": gm(a=None), "g_null_c": gm(c=None), "g_null_special": gm(fw=3, sp=None),
  "g_mixed": gm(fa=1, fw=0, K=64), "g_razer_w_a": gm(fa=3, fw=3, sp=ctypes.cast(SP, vp)),
- "g_bad_format": gm(fa=4), "g_K_block": gm(K=24), "g_K_mx": gm(fa=1, fw=1, K=48),
+ "g_bad_format": gm(fa=5), "g_ue5m3": gm(fa=4, fw=4), "g_ue5m3_w": gm(fa=0, fw=4), "g_K_block": gm(K=24), "g_K_mx": gm(fa=1, fw=1, K=48),
  "g_K_zero": gm(K=0), "g_M_neg": gm(M=-1), "g_ldc": gm(ldc=4), "g_align": gm(a=P + 4),
  "g_ldc_align": gm(ldc=9), "g_dtype": gm(ct=3), "g_K_big": gm(K=(1 << 24) + 16),
  "g_tiles": gm(M=1 << 40, N=1 << 40, ldc=1 << 40),
@@ -161,11 +164,13 @@ EXPECTED = {
     "q_x_align": 3, "q_ld_align": 3, "q_codes_align": 3, "q_chan_align": 3, "q_ld_align_bf16": 3,
     "q_bad_format": 4, "q_bad_struct": 5, "q_bad_block": 5, "q_mx_block": 5, "q_bad_rule": 5, "q_bad_flag": 5,
     "q_razer_rule": 5, "q_mx_rule": 5, "q_mx_pz": 5, "q_mx_global": 5, "q_bad_mode": 5, "q_bad_had": 5,
+    "q_had16_cols": 2, "q_ue5m3_auto": 5, "q_ue5m3_rule": 5, "q_nv_expsearch": 5, "q_bad_format5": 4,
     "q_bad_dtype": 5, "q_special_grid": 5, "q_special_half": 5, "q_special_big": 5, "q_special_zero": 5,
     "q_special_nan": 5,
     "dq_null_out": 1, "dq_null_codes": 1, "dq_shape": 2, "dq_ld": 2, "dq_align": 3, "dq_ld_align": 3,
     "dq_dtype": 5, "dq_format": 4, "dq_block": 5,
     "g_null_a": 1, "g_null_c": 1, "g_null_special": 1, "g_mixed": 4, "g_razer_w_a": 4, "g_bad_format": 4,
+    "g_ue5m3": 4, "g_ue5m3_w": 4,
     "g_K_block": 2, "g_K_mx": 2, "g_K_zero": 2, "g_M_neg": 2, "g_ldc": 2, "g_align": 3, "g_ldc_align": 3,
     "g_dtype": 5, "g_bad_special": 5, "g_K_big": 2, "g_tiles": 2,
     "gn_null_a": 1, "gn_mixed": 4, "gn_K_block": 2, "gn_align": 3, "gn_dtype": 5,
