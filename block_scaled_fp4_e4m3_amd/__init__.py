@@ -62,6 +62,7 @@ _SIGS = {
     "fp4q_gemm_w4a4_noalloc": (_int, [_int, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
                                       _i64, _vp]),
     "fp4q_channel_scale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp]),
+    "fp4q_macaq_quantize": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "fp4q_status_string": (ctypes.c_char_p, [_int]),
     "fp4q_abi_version": (_u32, []),
 }
@@ -188,6 +189,13 @@ def fp4q_gemm_w4a4_noalloc(fa, a_codes, a_scales, a_global, fw, w_codes, w_scale
                                        M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a4_noalloc")
 
 
+def fp4q_macaq_quantize(w, N: int, K: int, ldw: int, h, ldh: int, max_moves: int, codes, scales, moves,
+                        workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.fp4q_macaq_quantize(_ptr(w), N, K, ldw, _ptr(h), ldh, max_moves, _ptr(codes), _ptr(scales),
+                                    _ptr(moves), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "fp4q_macaq_quantize")
+
+
 def fp4q_channel_scale(x, x_dtype: int, rows_x: int, ldx: int, w, w_dtype: int, rows_w: int, ldw: int,
                        cols: int, alpha: float, t, r, stream=None) -> None:
     _check(_lib.fp4q_channel_scale(_ptr(x), x_dtype, rows_x, ldx, _ptr(w), w_dtype, rows_w, ldw, cols,
@@ -247,3 +255,18 @@ def channel_scale(x, w, alpha=0.75, stream=None):
     fp4q_channel_scale(x, _dtype_code(x), x.shape[0], x.stride(0), w, _dtype_code(w), w.shape[0], w.stride(0),
                        cols, alpha, t, r, stream)
     return t, r
+
+
+def macaq_quantize(w, h, max_moves=None, workspace_bytes=None, stream=None):
+    """MACaQ calibration of an fp32 CUDA weight (N x K) with a binary64 Hessian
+    (K x K).  Returns (codes, scales, moves per row)."""
+    import torch
+    N, K = w.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    moves = torch.empty(N, dtype=torch.int32, device=w.device)
+    wsb = workspace_bytes or max(8 * K, min(N, 4096) * 8 * K)
+    ws = torch.empty(wsb // 8, dtype=torch.float64, device=w.device)
+    fp4q_macaq_quantize(w, N, K, w.stride(0), h, h.stride(0), 2 * K if max_moves is None else max_moves,
+                        codes, scales, moves, ws, wsb, stream)
+    return codes, scales, moves

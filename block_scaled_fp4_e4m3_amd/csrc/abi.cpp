@@ -200,6 +200,29 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
   return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{scratch, kSplitWorkspaceBytes}));
 }
 
+fp4q_status fp4q_macaq_quantize(const float* w, int64_t N, int64_t K, int64_t ldw, const double* h,
+                                int64_t ldh, int64_t max_moves, uint8_t* codes, uint8_t* scales,
+                                int32_t* moves, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w || !h || !codes || !scales || !workspace) return FP4Q_ERR_NULL;
+  if (N < 0 || K <= 0 || K % 32 != 0 || K > macaq_max_k() || ldw < K || ldh < K) return FP4Q_ERR_SHAPE;
+  if (max_moves < 0 || workspace_bytes < (size_t)K * sizeof(double)) return FP4Q_ERR_ARG;
+  if (((uintptr_t)w & 3u) || ((uintptr_t)h & 7u) || ((uintptr_t)workspace & 7u) || ((uintptr_t)moves & 3u))
+    return FP4Q_ERR_ALIGN;
+  if (N == 0) return FP4Q_OK;
+  MacaqParams p{};
+  p.w = w;
+  p.N = N;
+  p.K = K;
+  p.ldw = ldw;
+  p.h = h;
+  p.ldh = ldh;
+  p.max_moves = max_moves;
+  p.codes = codes;
+  p.scales = scales;
+  p.moves = moves;
+  return device_status(launch_macaq(p, workspace, workspace_bytes, (hipStream_t)stream));
+}
+
 fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x, int64_t ldx,
                                const void* w, fp4q_dtype w_dtype, int64_t rows_w, int64_t ldw,
                                int64_t cols, double alpha, float* t, float* r, void* stream) {

@@ -50,6 +50,14 @@ struct GemmParams {
 // library's own array for the non-allocating entry point)
 constexpr size_t kSplitWorkspaceBytes = size_t(32) << 20;
 
+struct MacaqParams {
+  const float* w; int64_t N, K, ldw;      // weight, row n = output channel
+  const double* h; int64_t ldh;           // Hessian X^T X, K x K
+  int64_t max_moves;                      // per row
+  uint8_t* codes; uint8_t* scales;        // N x K/2, N x K/32
+  int32_t* moves;                         // N, or nullptr
+};
+
 struct ChanScaleParams {
   const void* x; int x_bf16; int64_t rows_x, ldx;
   const void* w; int w_bf16; int64_t rows_w, ldw;
@@ -76,6 +84,9 @@ float* split_workspace(hipStream_t s);
 // device (looked up once per device), or nullptr if the lookup failed
 float* noalloc_scratch();
 hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s);
+// MACaQ calibration; workspace holds the r rows of one pass (K doubles per row)
+hipError_t launch_macaq(const MacaqParams& p, void* workspace, size_t ws_bytes, hipStream_t s);
+int64_t macaq_max_k();
 
 // compile-time loop: f(std::integral_constant<int, I>) for I in [B, E); used
 // where a builtin needs an immediate operand (the FP4 convert's byte select)

@@ -51,6 +51,7 @@
 #ifndef FP4Q_H
 #define FP4Q_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -221,6 +222,41 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
 fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x, int64_t ldx,
                                const void* w, fp4q_dtype w_dtype, int64_t rows_w, int64_t ldw,
                                int64_t cols, double alpha, float* t, float* r, void* stream);
+
+/*
+ * MACaQ weight calibration for MXFP4 (MACaQ review, sections 1 and 3): the
+ * weight's codes and E8M0 exponents chosen for the layer-output error
+ * ||X W^T - X W^^T||_F^2 = sum_n (w_n - w^_n)^T H (w_n - w^_n), H = X^T X.
+ *   1. Hessian-weighted exponent screening: per 32-element block, the
+ *      standard exponent E (as fp4q_quantize's MXFP4) and E + 1, E - 1, in
+ *      that order, each with round-to-nearest codes, compared by e^T H_bb e
+ *      (H_bb the block's 32 x 32 diagonal block of H, e the block error); the
+ *      strictly smallest is kept.
+ *   2. Flip-Refinement: per row, repeatedly the single move of one code to
+ *      an adjacent E2M1 level with the largest gain
+ *      -(2 delta (H d)_k + delta^2 H_kk) (d = w^ - w) is taken while the gain
+ *      is positive (a tie keeps the smaller k, then the move up), at most
+ *      max_moves times; H d is updated by delta times row k of H.
+ * All arithmetic is binary64 in a fixed order: every sum over j runs j
+ * ascending; e^T H_bb e adds the 32 products e_i (H_bb e)_i by a balanced
+ * pairwise tree in index order; the gain is -(2 (delta r_k) + (delta delta)
+ * H_kk).  The weight is taken as given: apply any channel scale or rotation
+ * (W D^-1 B) before, and pass the Hessian of the transformed activations.
+ *   w          device fp32, N x K, row pitch ldw (row n = output channel)
+ *   h          device binary64, K x K, row pitch ldh (rows are read)
+ *   codes      device, N x K/2 (layout as fp4q_quantize), written
+ *   scales     device, N x K/32 E8M0 codes, written
+ *   moves      device int32 per row (moves taken), or NULL
+ *   workspace  device, 8-byte aligned; holds H d for workspace_bytes / (8 K)
+ *              rows at a time (at least one row: 8 K bytes)
+ * Errors: NULL pointer -> ERR_NULL; N < 0, K <= 0, K % 32, K > 5120,
+ * ldw < K or ldh < K -> ERR_SHAPE; max_moves < 0 or a workspace below one
+ * row -> ERR_ARG; misaligned w (4), h, workspace (8), moves (4) -> ERR_ALIGN.
+ * N == 0 enqueues nothing.
+ */
+fp4q_status fp4q_macaq_quantize(const float* w, int64_t N, int64_t K, int64_t ldw, const double* h,
+                                int64_t ldh, int64_t max_moves, uint8_t* codes, uint8_t* scales,
+                                int32_t* moves, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* fp4q_status_string(fp4q_status s);

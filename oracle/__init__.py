@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "or_gemm_rows": (i, [i, vp, vp, f, i, vp, vp, f, vp, l, l, l, l, l, vp]),
             "or_gemm_entries": (i, [i, vp, vp, f, i, vp, vp, f, vp, l, l, l, vp, vp, l, vp]),
             "or_channel_scale": (None, [vp, i, l, l, vp, i, l, l, l, d, vp, vp]),
+            "or_macaq_quantize": (i, [vp, l, l, l, vp, l, l, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -233,3 +234,22 @@ def channel_scale(x: np.ndarray, w: np.ndarray, alpha: float = 0.75):
     r = np.empty(cols, np.float32)
     lib().or_channel_scale(_p(x), dx, x.shape[0], cols, _p(w), dw, w.shape[0], cols, cols, alpha, _p(t), _p(r))
     return t, r
+
+
+def macaq_quantize(w: np.ndarray, h: np.ndarray, max_moves: int | None = None):
+    """MACaQ weight calibration of W (N x K fp32) with the Hessian H (K x K
+    binary64): screened exponents and Flip-Refinement.  Returns (codes,
+    scales, moves per row, objective before/after per row)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    N, K = w.shape
+    assert h.shape == (K, K)
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    moves = np.empty(N, np.int32)
+    obj = np.empty((N, 2), np.float64)
+    mm = 2 * K if max_moves is None else max_moves
+    rc = lib().or_macaq_quantize(_p(w), N, K, K, _p(h), K, mm, _p(codes), _p(scales), _p(moves), _p(obj))
+    if rc:
+        raise ValueError("or_macaq_quantize rejected the arguments")
+    return codes, scales, moves, obj

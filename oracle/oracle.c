@@ -554,3 +554,140 @@ void or_channel_scale(const void* x, int xdtype, long rows_x, long ldx,
     r[j] = 1.0f / t[j];
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* MACaQ weight calibration                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* The 15 distinct E2M1 values in increasing order, with their codes; a code's
+ * adjacent levels are its neighbours in this list ([MACaQ] section 1:
+ * Flip-Refinement moves a code to the immediately adjacent E2M1 level). */
+static const double LEVELS[15] = {-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6};
+static const int LEVEL_CODE[15] = {15, 14, 13, 12, 11, 10, 9, 0, 1, 2, 3, 4, 5, 6, 7};
+
+static int level_of(int code) {
+  for (int i = 0; i < 15; ++i)
+    if (LEVEL_CODE[i] == code || (code == 8 && i == 7)) return i;
+  return 7;
+}
+
+/* Hessian-weighted error of one block: e_i = x_i - v_i 2^E (exact in
+ * binary64), u_i = sum_j H[i][j] e_j with j ascending, then the balanced
+ * pairwise tree (index order) of e_i u_i, every step a binary64 operation. */
+static double block_hcost(const float* x, const int* codes, int E, const double* hbb, long ldh) {
+  double e[32], p[32];
+  for (int i = 0; i < 32; ++i) e[i] = (double)x[i] - or_e2m1_value(codes[i]) * ldexp(1.0, E);
+  for (int i = 0; i < 32; ++i) {
+    double u = 0.0;
+    for (int j = 0; j < 32; ++j) u = u + hbb[i * ldh + j] * e[j];
+    p[i] = e[i] * u;
+  }
+  for (int n = 32; n > 1; n /= 2)   /* balanced tree: T(0..n) = T(left) + T(right) */
+    for (int i = 0; i < n / 2; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+  return p[0];
+}
+
+int or_macaq_quantize(const float* w, long N, long K, long ldw, const double* h, long ldh,
+                      long max_moves, uint8_t* codes, uint8_t* scales, int* moves,
+                      double* objective) {
+  if (N < 0 || K <= 0 || K % 32 || ldw < K || ldh < K || max_moves < 0) return -1;
+  int* cd = (int*)malloc(sizeof(int) * (size_t)K);
+  int* ex = (int*)malloc(sizeof(int) * (size_t)(K / 32));
+  double* d = (double*)malloc(sizeof(double) * (size_t)K);
+  double* r = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!cd || !ex || !d || !r) { free(cd); free(ex); free(d); free(r); return -2; }
+  for (long n = 0; n < N; ++n) {
+    const float* x = w + n * ldw;
+    /* 1. exponent screening, per block: candidates E, E+1, E-1 in that order,
+     * the strictly smallest Hessian-weighted error kept */
+    for (long b = 0; b < K / 32; ++b) {
+      const float* xb = x + 32 * b;
+      const double* hbb = h + (32 * b) * ldh + 32 * b;
+      double a = block_absmax(xb, 32);
+      int E = (a == 0.0) ? -127 : floor_log2(a) - 2;
+      if (E < -127) E = -127;
+      if (E > 127) E = 127;
+      int best_c[32], tmp[32];
+      encode_plain(xb, 32, ldexp(1.0, E), 1.0, best_c);
+      double best = block_hcost(xb, best_c, E, hbb, ldh);
+      int bestE = E;
+      const int off[2] = {1, -1};
+      for (int t = 0; t < 2; ++t) {
+        int Ec = E + off[t];
+        if (Ec < -127 || Ec > 127) continue;
+        encode_plain(xb, 32, ldexp(1.0, Ec), 1.0, tmp);
+        double c = block_hcost(xb, tmp, Ec, hbb, ldh);
+        if (c < best) {
+          best = c;
+          bestE = Ec;
+          memcpy(best_c, tmp, sizeof(best_c));
+        }
+      }
+      ex[b] = bestE;
+      for (int i = 0; i < 32; ++i) cd[32 * b + i] = best_c[i];
+    }
+    /* 2. Flip-Refinement on f = d^T H d, d = w^ - w: r = H d (j ascending);
+     * a move of code k by one level changes w^_k by delta and f by
+     * 2 delta r_k + delta^2 H_kk; its gain is the negative of that.  The
+     * largest gain wins (k ascending, the move up before the move down, a
+     * tie keeps the earlier); it is taken while it is positive. */
+    for (long k = 0; k < K; ++k) d[k] = or_e2m1_value(cd[k]) * ldexp(1.0, ex[k / 32]) - (double)x[k];
+    for (long k = 0; k < K; ++k) {
+      double s = 0.0;
+      for (long j = 0; j < K; ++j) s = s + h[k * ldh + j] * d[j];
+      r[k] = s;
+    }
+    double f0 = 0.0;
+    if (objective)
+      for (long k = 0; k < K; ++k) f0 = f0 + d[k] * r[k];
+    long taken = 0;
+    while (taken < max_moves) {
+      double best = 0.0;
+      long bk = -1;
+      double bdelta = 0.0;
+      int blevel = 0;
+      for (long k = 0; k < K; ++k) {
+        const int lv = level_of(cd[k]);
+        const double sc = ldexp(1.0, ex[k / 32]);
+        for (int dir = 0; dir < 2; ++dir) {
+          const int nl = dir == 0 ? lv + 1 : lv - 1;
+          if (nl < 0 || nl > 14) continue;
+          const double delta = (LEVELS[nl] - LEVELS[lv]) * sc;
+          const double t1 = delta * r[k];
+          const double t2 = delta * delta;
+          const double q = 2.0 * t1 + t2 * h[k * ldh + k];
+          const double gain = -q;
+          if (gain > best) {
+            best = gain;
+            bk = k;
+            bdelta = delta;
+            blevel = nl;
+          }
+        }
+      }
+      if (bk < 0) break;   /* no move gains: the row leaves the active set */
+      cd[bk] = LEVEL_CODE[blevel];
+      for (long j = 0; j < K; ++j) r[j] = r[j] + bdelta * h[bk * ldh + j];
+      ++taken;
+    }
+    if (moves) moves[n] = (int)taken;
+    if (objective) {
+      double f1 = 0.0;
+      for (long k = 0; k < K; ++k) d[k] = or_e2m1_value(cd[k]) * ldexp(1.0, ex[k / 32]) - (double)x[k];
+      for (long k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (long j = 0; j < K; ++j) s = s + h[k * ldh + j] * d[j];
+        f1 = f1 + d[k] * s;
+      }
+      objective[2 * n] = f0;
+      objective[2 * n + 1] = f1;
+    }
+    for (long b = 0; b < K / 32; ++b) scales[n * (K / 32) + b] = (uint8_t)(ex[b] + 127);
+    for (long k = 0; k < K; k += 2) codes[n * (K / 2) + k / 2] = (uint8_t)(cd[k] | (cd[k + 1] << 4));
+  }
+  free(cd);
+  free(ex);
+  free(d);
+  free(r);
+  return 0;
+}

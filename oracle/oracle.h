@@ -129,6 +129,23 @@ int or_gemm_entries(int fa, const uint8_t* a_codes, const uint8_t* a_scales, flo
                     const float* w_special4, long M, long N, long K, const long* ms,
                     const long* ns, long count, float* out);
 
+/* MACaQ weight calibration for MXFP4 ([MACaQ] sections 1 and 3): for each
+ * row of W (N x K, row n = output channel, fp32) and the layer-input Hessian
+ * H = X^T X (K x K, binary64, row-major, pitch ldh):
+ *  1. exponent screening: per 32-element block the standard exponent E and
+ *     E + 1, E - 1 are compared by the Hessian-weighted error e^T H_bb e of
+ *     the block's RTN codes (H_bb the block's 32 x 32 diagonal block);
+ *  2. Flip-Refinement: starting from the screened RTN codes, the single move
+ *     of one code to an adjacent E2M1 level with the largest gain in
+ *     f = (w - w^)^T H (w - w^) is taken, repeatedly, while a move gains
+ *     (at most max_moves per row).
+ * Writes codes (N x K/2), scales (E8M0 codes, N x K/32); moves[n] = moves
+ * taken on row n and objective[2n], [2n+1] = f before and after refinement
+ * (either may be NULL).  Returns 0, or -1 on a bad argument. */
+int or_macaq_quantize(const float* w, long N, long K, long ldw, const double* h, long ldh,
+                      long max_moves, uint8_t* codes, uint8_t* scales, int* moves,
+                      double* objective);
+
 /* per-channel scale t_j = (rms_j(W) / rms_j(X))^alpha in binary64, rounded to
  * fp32, and r_j = RN32(1 / t_j).  X is rows_x x cols, W is rows_w x cols. */
 void or_channel_scale(const void* x, int xdtype, long rows_x, long ldx,

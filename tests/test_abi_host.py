@@ -78,6 +78,7 @@ L.fp4q_dequantize.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, i64, vp, ci
 L.fp4q_gemm_w4a4.argtypes = [ci, vp, vp, vp, ci, vp, vp, vp, vp, i64, i64, i64, vp, ci, i64, vp]
 L.fp4q_gemm_w4a4_noalloc.argtypes = L.fp4q_gemm_w4a4.argtypes
 L.fp4q_channel_scale.argtypes = [vp, ci, i64, i64, vp, ci, i64, i64, i64, ctypes.c_double, vp, vp, vp]
+L.fp4q_macaq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
 P = 0x100000  # aligned fake device address; never dereferenced on any error path
 
 def desc(**kw):
@@ -105,6 +106,9 @@ def gm(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc
 
 def gn(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc=8):
     return L.fp4q_gemm_w4a4_noalloc(fa, a, sa, None, fw, w, sw, None, sp, M, N, K, c, ct, ldc, None)
+
+def mq(w=P, N=4, K=64, ldw=64, h=P, ldh=64, mm=10, codes=P, scales=P, moves=None, ws=P, wsb=1 << 20):
+    return L.fp4q_macaq_quantize(w, N, K, ldw, h, ldh, mm, codes, scales, moves, ws, wsb, None)
 
 def cs(x=P, rows_x=4, ldx=8, w=P, rows_w=4, ldw=8, cols=8, alpha=0.75, t=P, r=P):
     return L.fp4q_channel_scale(x, 0, rows_x, ldx, w, 0, rows_w, ldw, cols, alpha, t, r, None)
@@ -151,6 +155,9 @@ res = {
  # the non-allocating matmul: the same checks
  "gn_null_a": gn(a=None), "gn_mixed": gn(fa=1, fw=0), "gn_K_block": gn(K=24), "gn_align": gn(c=P + 4),
  "gn_dtype": gn(ct=3),
+ # MACaQ calibration
+ "m_null_w": mq(w=None), "m_null_ws": mq(ws=None), "m_K": mq(K=48, ldw=64), "m_K_big": mq(K=5152, ldw=5152, ldh=5152),
+ "m_ldh": mq(ldh=32), "m_N": mq(N=-1), "m_moves": mq(mm=-1), "m_ws": mq(wsb=8 * 64 - 8), "m_align": mq(h=P + 4),
  # channel scale
  "c_null": cs(t=None), "c_rows": cs(rows_x=0), "c_ld": cs(ldx=4), "c_alpha": cs(alpha=float("inf")),
 }
@@ -174,6 +181,8 @@ EXPECTED = {
     "g_K_block": 2, "g_K_mx": 2, "g_K_zero": 2, "g_M_neg": 2, "g_ldc": 2, "g_align": 3, "g_ldc_align": 3,
     "g_dtype": 5, "g_bad_special": 5, "g_K_big": 2, "g_tiles": 2,
     "gn_null_a": 1, "gn_mixed": 4, "gn_K_block": 2, "gn_align": 3, "gn_dtype": 5,
+    "m_null_w": 1, "m_null_ws": 1, "m_K": 2, "m_K_big": 2, "m_ldh": 2, "m_N": 2, "m_moves": 5, "m_ws": 5,
+    "m_align": 3,
     "c_null": 1, "c_rows": 2, "c_ld": 2, "c_alpha": 5,
 }
 
@@ -193,8 +202,8 @@ def test_zero_rows_and_empty_gemm_enqueue_nothing():
     # with no visible device
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     code = f"ROOT = {ROOT!r}\nLIB = {LIB!r}\n" + CHILD.split("res = {")[0] + textwrap.dedent('''
-print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0))
+print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0), mq(N=0))
 ''')
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == ["0", "0", "0", "0", "0", "0"]
+    assert out.stdout.split() == ["0"] * 7
