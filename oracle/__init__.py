@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
             "or_gemm_entries": (i, [i, vp, vp, f, i, vp, vp, f, vp, l, l, l, vp, vp, l, vp]),
             "or_channel_scale": (None, [vp, i, l, l, vp, i, l, l, l, d, vp, vp]),
             "or_macaq_quantize": (i, [vp, l, l, l, vp, l, l, vp, vp, vp, vp]),
+            "or_gemm_w4a16_rows": (i, [vp, l, i, vp, vp, f, vp, l, l, l, l, l, vp]),
+            "or_razer_table_search": (i, [vp, i, l, l, l, f, vp]),
+            "or_razer_pair": (None, [i, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -253,3 +256,38 @@ def macaq_quantize(w: np.ndarray, h: np.ndarray, max_moves: int | None = None):
     if rc:
         raise ValueError("or_macaq_quantize rejected the arguments")
     return codes, scales, moves, obj
+
+
+def gemm_w4a16_rows(a_bf16: np.ndarray, fw, w_codes, w_scales, g_w, w_special, N, m0=0, m1=None) -> np.ndarray:
+    """C = g_w A W^^T for A in bf16 bits (M x K) and W as codes/scales (block 16)."""
+    a = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    M, K = a.shape
+    m1 = M if m1 is None else m1
+    out = np.empty((m1 - m0, N), np.float32)
+    w_codes, w_scales = np.ascontiguousarray(w_codes), np.ascontiguousarray(w_scales)
+    sp = _special(w_special)
+    rc = lib().or_gemm_w4a16_rows(_p(a), K, _fmt(fw), _p(w_codes), _p(w_scales), g_w, _p(sp), M, N, K, m0, m1,
+                                  _p(out))
+    if rc:
+        raise ValueError("or_gemm_w4a16_rows rejected the arguments")
+    return out
+
+
+RAZER_NPAIRS = 28
+
+
+def razer_pair(p: int):
+    a, b = ctypes.c_float(), ctypes.c_float()
+    lib().or_razer_pair(p, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def razer_table_search(x: np.ndarray, g: float):
+    """Tensor error of every special-value pair and the index of the best."""
+    x, dt = _x_and_dtype(x)
+    rows, cols = x.shape
+    sse = np.empty(RAZER_NPAIRS, np.float64)
+    best = lib().or_razer_table_search(_p(x), dt, rows, cols, cols, g, _p(sse))
+    if best < 0:
+        raise ValueError("or_razer_table_search rejected the arguments")
+    return sse, best

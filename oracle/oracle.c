@@ -556,6 +556,88 @@ void or_channel_scale(const void* x, int xdtype, long rows_x, long ldx,
 }
 
 /* ------------------------------------------------------------------------- */
+/* RaZeR weight-only matmul and the offline special-value search              */
+/* ------------------------------------------------------------------------- */
+
+int or_gemm_w4a16_rows(const uint16_t* a, long lda, int fw, const uint8_t* w_codes,
+                       const uint8_t* w_scales, float g_w, const float* w_special4,
+                       long M, long N, long K, long m0, long m1, float* c) {
+  if ((fw != OR_NVFP4 && fw != OR_RAZER_W) || K <= 0 || K % 16 || m0 < 0 || m1 > M || m0 > m1 || lda < K)
+    return -1;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!wd) return -2;
+  for (long n = 0; n < N; ++n) {
+    or_decode_row(fw, 16, w_special4, w_codes + n * (K / 2), w_scales + n * (K / 16), K, wd);
+    for (long m = m0; m < m1; ++m) {
+      double acc = 0.0;
+      for (long k = 0; k < K; ++k) acc += (double)load_elem(a, OR_BF16, m * lda + k) * wd[k];
+      c[(m - m0) * N + n] = (float)((double)g_w * acc);
+    }
+  }
+  free(wd);
+  return 0;
+}
+
+static const float RAZER_CAND[OR_RAZER_NCAND] = {2.5f, 3.5f, 4.5f, 5.0f, 5.5f, 6.5f, 7.0f, 7.5f};
+
+void or_razer_pair(int p, float* a, float* b) {
+  int q = 0;
+  for (int i = 0; i < OR_RAZER_NCAND; ++i)
+    for (int j = i + 1; j < OR_RAZER_NCAND; ++j, ++q)
+      if (q == p) {
+        *a = RAZER_CAND[i];
+        *b = RAZER_CAND[j];
+      }
+}
+
+int or_razer_table_search(const void* x, int xdtype, long rows, long cols, long ld, float g,
+                          double* pair_sse) {
+  if (rows < 0 || cols <= 0 || cols % 16 || ld < cols) return -1;
+  float* xr = (float*)malloc(sizeof(float) * (size_t)cols);
+  double* row_sum = (double*)malloc(sizeof(double) * OR_RAZER_NPAIRS);
+  if (!xr || !row_sum) { free(xr); free(row_sum); return -2; }
+  for (int p = 0; p < OR_RAZER_NPAIRS; ++p) pair_sse[p] = 0.0;
+  for (long r = 0; r < rows; ++r) {
+    for (long j = 0; j < cols; ++j) xr[j] = load_elem(x, xdtype, r * ld + j);
+    for (int p = 0; p < OR_RAZER_NPAIRS; ++p) row_sum[p] = 0.0;
+    for (long b = 0; b < cols / 16; ++b) {
+      const float* xb = xr + 16 * b;
+      /* the RaZeR-W block scale (abs-max E3M3) and the error of each signed
+       * candidate as the block's special value */
+      int k = or_round_scale(OR_SF_E3M3, block_absmax(xb, 16), 6.0, (double)g);
+      double s = or_e3m3_value(k);
+      float err[2 * OR_RAZER_NCAND];
+      int codes[16];
+      for (int c = 0; c < 2 * OR_RAZER_NCAND; ++c) {
+        double v = (c & 1) ? -RAZER_CAND[c / 2] : RAZER_CAND[c / 2];
+        if (k == 0) {
+          for (int i = 0; i < 16; ++i) codes[i] = 0;
+        } else {
+          encode_special(xb, 16, s, (double)g, v, codes);
+        }
+        err[c] = or_block_sse(xb, codes, 16, s, g, 1, v);
+      }
+      int p = 0;
+      for (int i = 0; i < OR_RAZER_NCAND; ++i)
+        for (int j = i + 1; j < OR_RAZER_NCAND; ++j, ++p) {
+          float m = err[2 * i];
+          if (err[2 * i + 1] < m) m = err[2 * i + 1];
+          if (err[2 * j] < m) m = err[2 * j];
+          if (err[2 * j + 1] < m) m = err[2 * j + 1];
+          row_sum[p] = row_sum[p] + (double)m;
+        }
+    }
+    for (int p = 0; p < OR_RAZER_NPAIRS; ++p) pair_sse[p] = pair_sse[p] + row_sum[p];
+  }
+  int best = 0;
+  for (int p = 1; p < OR_RAZER_NPAIRS; ++p)
+    if (pair_sse[p] < pair_sse[best]) best = p;
+  free(xr);
+  free(row_sum);
+  return best;
+}
+
+/* ------------------------------------------------------------------------- */
 /* MACaQ weight calibration                                                   */
 /* ------------------------------------------------------------------------- */
 

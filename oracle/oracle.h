@@ -129,6 +129,30 @@ int or_gemm_entries(int fa, const uint8_t* a_codes, const uint8_t* a_scales, flo
                     const float* w_special4, long M, long N, long K, const long* ms,
                     const long* ns, long count, float* out);
 
+/* RaZeR weight-only matmul ([RaZeR] 2.3, W4A16): C = g_w * A W^^T for rows
+ * [m0, m1) with A in bf16 (bit patterns, M x K, pitch lda) and W (N x K) given
+ * as codes/scales of format fw (NVFP4 or RaZeR-W, block 16).  Accumulates the
+ * exact products in binary64, then C = RN32(g_w * acc). */
+int or_gemm_w4a16_rows(const uint16_t* a, long lda, int fw, const uint8_t* w_codes,
+                       const uint8_t* w_scales, float g_w, const float* w_special4,
+                       long M, long N, long K, long m0, long m1, float* c);
+
+/* RaZeR offline special-value search ([RaZeR] 2.2): the candidate magnitudes
+ * are the multiples of 0.5 in (0, 7.5] that are not E2M1 magnitudes,
+ * {2.5, 3.5, 4.5, 5, 5.5, 6.5, 7, 7.5}; a table is {+a, -a, +b, -b} for a pair
+ * a < b (28 pairs, lexicographic).  For a table, each 16-element block of the
+ * weight (RaZeR-W: abs-max E3M3 scale under g) takes the table value with the
+ * smallest block error (or_block_sse), and the tensor error is the binary64
+ * sum over rows (ascending) of the binary64 sum over the row's blocks
+ * (ascending).  Writes the 28 tensor errors and returns the index of the
+ * smallest (a tie keeps the earlier pair), or -1 on a bad argument. */
+#define OR_RAZER_NCAND 8
+#define OR_RAZER_NPAIRS 28
+int or_razer_table_search(const void* x, int xdtype, long rows, long cols, long ld, float g,
+                          double* pair_sse);
+/* magnitudes of pair p (0 .. 27) */
+void or_razer_pair(int p, float* a, float* b);
+
 /* MACaQ weight calibration for MXFP4 ([MACaQ] sections 1 and 3): for each
  * row of W (N x K, row n = output channel, fp32) and the layer-input Hessian
  * H = X^T X (K x K, binary64, row-major, pitch ldh):
