@@ -63,6 +63,9 @@ _SIGS = {
                                       _i64, _vp]),
     "fp4q_channel_scale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp]),
     "fp4q_macaq_quantize": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "fp4q_gemm_w4a16": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _i64, _vp]),
+    "fp4q_razer_table_search": (_int, [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                       _vp]),
     "fp4q_status_string": (ctypes.c_char_p, [_int]),
     "fp4q_abi_version": (_u32, []),
 }
@@ -196,6 +199,23 @@ def fp4q_macaq_quantize(w, N: int, K: int, ldw: int, h, ldh: int, max_moves: int
            "fp4q_macaq_quantize")
 
 
+def fp4q_gemm_w4a16(a, lda: int, fw, w_codes, w_scales, w_global, w_special, M: int, N: int, K: int, c,
+                    c_dtype: int, ldc: int, stream=None) -> None:
+    sp = None
+    if w_special is not None:
+        sp = (ctypes.c_float * 4)(*[float(v) for v in w_special])
+    _check(_lib.fp4q_gemm_w4a16(_ptr(a), lda, _fmt(fw), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                ctypes.cast(sp, ctypes.c_void_p) if sp is not None else None,
+                                M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a16")
+
+
+def fp4q_razer_table_search(w, w_dtype: int, rows: int, cols: int, ld_w: int, global_mode, global_, pair_sse,
+                            table, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.fp4q_razer_table_search(_ptr(w), w_dtype, rows, cols, ld_w, _gmode(global_mode), _ptr(global_),
+                                        _ptr(pair_sse), _ptr(table), _ptr(workspace), workspace_bytes,
+                                        _stream(stream)), "fp4q_razer_table_search")
+
+
 def fp4q_channel_scale(x, x_dtype: int, rows_x: int, ldx: int, w, w_dtype: int, rows_w: int, ldw: int,
                        cols: int, alpha: float, t, r, stream=None) -> None:
     _check(_lib.fp4q_channel_scale(_ptr(x), x_dtype, rows_x, ldx, _ptr(w), w_dtype, rows_w, ldw, cols,
@@ -270,3 +290,35 @@ def macaq_quantize(w, h, max_moves=None, workspace_bytes=None, stream=None):
     fp4q_macaq_quantize(w, N, K, w.stride(0), h, h.stride(0), 2 * K if max_moves is None else max_moves,
                         codes, scales, moves, ws, wsb, stream)
     return codes, scales, moves
+
+
+def gemm_w4a16(a, fw, w_codes, w_scales, w_global=None, w_special=None, out_dtype=None, out=None, stream=None):
+    """C = g_w A W^^T for bf16 activations A [M, K] and a block-16 NVFP4 or
+    RaZeR-W weight W^ [N, K/2]."""
+    import torch
+    if a.dtype != torch.bfloat16 or a.stride(1) != 1:
+        raise ValueError("a must be bf16 with unit stride along its last dimension")
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    fp4q_gemm_w4a16(a, a.stride(0), fw, w_codes, w_scales, w_global, w_special, M, N, K, out, _dtype_code(out),
+                    out.stride(0), stream)
+    return out
+
+
+def razer_table_search(w, global_mode="auto", global_=None, stream=None):
+    """RaZeR-W special-value search over a CUDA weight (fp32/bf16, rows x
+    cols).  Returns (table fp32 [4], errors of the 28 pairs fp64 [28], global
+    fp32 [1])."""
+    import torch
+    rows, cols = w.shape
+    dev = w.device
+    if global_ is None:
+        global_ = torch.ones(1, dtype=torch.float32, device=dev)
+    pair_sse = torch.empty(28, dtype=torch.float64, device=dev)
+    table = torch.empty(4, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(rows, 1) * 28, dtype=torch.float64, device=dev)
+    fp4q_razer_table_search(w, _dtype_code(w), rows, cols, w.stride(0), global_mode, global_, pair_sse, table, ws,
+                            ws.numel() * 8, stream)
+    return table, pair_sse, global_

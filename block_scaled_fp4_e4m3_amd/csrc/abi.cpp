@@ -200,6 +200,66 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
   return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{scratch, kSplitWorkspaceBytes}));
 }
 
+fp4q_status fp4q_gemm_w4a16(const uint16_t* a, int64_t lda, fp4q_format fw, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* w_global, const float* w_special, int64_t M,
+                            int64_t N, int64_t K, void* c, fp4q_dtype c_dtype, int64_t ldc, void* stream) {
+  if (fw != FP4Q_NVFP4 && fw != FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
+  if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!a || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
+  if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
+  if (M < 0 || N < 0 || K <= 0 || K % 512 != 0 || K > (int64_t(1) << 24) || lda < K || lda > (int64_t(1) << 24) ||
+      ldc < N)
+    return FP4Q_ERR_SHAPE;
+  if (fw == FP4Q_NVFP4_RAZER_W)
+    for (int i = 0; i < 4; ++i)
+      if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
+  if (!aligned16(a) || lda % 8 != 0 || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(c) ||
+      (ldc * (int64_t)elem_size(c_dtype)) % 16 != 0)
+    return FP4Q_ERR_ALIGN;
+  if (w_global && ((uintptr_t)w_global & 3u)) return FP4Q_ERR_ALIGN;
+  if (M == 0 || N == 0) return FP4Q_OK;
+  GemmParams p{};
+  p.a_bf16 = a;
+  p.lda = lda;
+  p.w_codes = w_codes;
+  p.w_scales = w_scales;
+  p.w_global = w_global;
+  for (int i = 0; i < 4; ++i) p.w_special[i] = (fw == FP4Q_NVFP4_RAZER_W) ? w_special[i] : 0.0f;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  p.c_bf16 = c_dtype == FP4Q_BF16;
+  return device_status(launch_gemm_w4a16(fw, p, (hipStream_t)stream, Workspace{nullptr, kSplitWorkspaceBytes}));
+}
+
+fp4q_status fp4q_razer_table_search(const void* w, fp4q_dtype w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                                    fp4q_global_mode global_mode, float* global, double* pair_sse, float* table,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (w_dtype != FP4Q_F32 && w_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (global_mode < FP4Q_GLOBAL_NONE || global_mode > FP4Q_GLOBAL_GIVEN) return FP4Q_ERR_ARG;
+  if (!pair_sse || !table) return FP4Q_ERR_NULL;
+  if (global_mode != FP4Q_GLOBAL_NONE && !global) return FP4Q_ERR_NULL;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld_w < cols) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && (!w || !workspace)) return FP4Q_ERR_NULL;
+  if ((uint64_t)rows > (uint64_t)(SIZE_MAX / (kRazerPairs * sizeof(double))) ||
+      workspace_bytes < (size_t)rows * kRazerPairs * sizeof(double))
+    return FP4Q_ERR_ARG;
+  if (!aligned16(w) || (ld_w * (int64_t)elem_size(w_dtype)) % 16 != 0) return FP4Q_ERR_ALIGN;
+  if (((uintptr_t)pair_sse & 7u) || ((uintptr_t)table & 3u) || ((uintptr_t)workspace & 7u) ||
+      (global && ((uintptr_t)global & 3u)))
+    return FP4Q_ERR_ALIGN;
+  QuantParams p{};
+  p.x = w;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld_w;
+  p.x_bf16 = w_dtype == FP4Q_BF16;
+  p.global = global_mode == FP4Q_GLOBAL_NONE ? nullptr : global;
+  return device_status(launch_razer_search(p, global_mode, (double*)workspace, pair_sse, table, (hipStream_t)stream));
+}
+
 fp4q_status fp4q_macaq_quantize(const float* w, int64_t N, int64_t K, int64_t ldw, const double* h,
                                 int64_t ldh, int64_t max_moves, uint8_t* codes, uint8_t* scales,
                                 int32_t* moves, void* workspace, size_t workspace_bytes, void* stream) {

@@ -42,6 +42,7 @@ struct GemmParams {
   float w_special[4];
   int64_t M, N, K;
   void* c; int64_t ldc; int c_bf16;
+  const uint16_t* a_bf16; int64_t lda;  // weight-only matmul: bf16 activations (M x K, pitch lda)
   int splits;       // K-splits per output tile (set by the launcher)
   float* partials;  // splits > 1: the splits' RN32(g * acc_s), dense M x N slices, added in split order
 };
@@ -77,6 +78,9 @@ struct Workspace {
   size_t bytes;
 };
 hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s, const Workspace& ws);
+// weight-only matmul (bf16 activations in p.a_bf16), fw NVFP4 or RAZER_W;
+// needs K % 512 == 0 and 16-byte aligned rows
+hipError_t launch_gemm_w4a16(int fw, const GemmParams& p, hipStream_t s, const Workspace& ws);
 // the split-K workspace of stream s on the current device (allocated on first
 // use, kept until the process ends), or nullptr
 float* split_workspace(hipStream_t s);
@@ -84,6 +88,11 @@ float* split_workspace(hipStream_t s);
 // device (looked up once per device), or nullptr if the lookup failed
 float* noalloc_scratch();
 hipError_t launch_channel_scale(const ChanScaleParams& p, hipStream_t s);
+constexpr int kRazerPairs = 28;  // special-value pairs the search compares
+// RaZeR special-value search over p.x (rows x cols, block 16) under *p.global
+// (AUTO: computed first); row_sums: rows x 28 doubles of workspace
+hipError_t launch_razer_search(const QuantParams& p, int gmode, double* row_sums, double* pair_sse, float* table,
+                               hipStream_t s);
 // MACaQ calibration; workspace holds the r rows of one pass (K doubles per row)
 hipError_t launch_macaq(const MacaqParams& p, void* workspace, size_t ws_bytes, hipStream_t s);
 int64_t macaq_max_k();

@@ -52,6 +52,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -1465,17 +1466,71 @@ __device__ __forceinline__ void sm_decode(const uint4& c, uint32_t sc, uint32_t 
   });
 }
 
+// The weight-only path: the lane's 32 codes of a chunk as bf16 (four words of
+// 8), exactly.  value * scale has at most 8 significant bits (E2M1 value 2,
+// special value 4, E4M3 / E3M3 scale 4), so the FP32 product is a bf16
+// number and its upper half is the bf16 pattern.  RaZeR-W: code 0x8 stands
+// for the block's special value; a second convert of a word with +1.0 exactly
+// at those codes gives u, and fma(u, special * scale, value * scale) is
+// special * scale there (value * scale = -0) and value * scale elsewhere.
+// sc: the lane's two scale bytes (blocks of words 0-1 and 2-3).
+__device__ __forceinline__ float e3m3_f32(uint32_t k) {
+  const uint32_t e = k >> 3, m = k & 7u;
+  return e == 0 ? (float)m * 0x1p-5f : __uint_as_float(((e + 124u) << 23) | (m << 20));
+}
+
+template <int F>
+__device__ __forceinline__ void sm_decode_bf16(const uint4& c, uint32_t sc, const float* special, uint4 (&out)[4]) {
+  float s[2], sp[2] = {0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t b = (sc >> (8 * h)) & 0xFFu;
+    if constexpr (F == RAZER_W) {
+      s[h] = e3m3_f32(b & 0x3Fu);
+      sp[h] = special[b >> 6] * s[h];  // exact
+    } else {
+      s[h] = __builtin_amdgcn_cvt_scalef32_f32_fp8(b & 0x7Fu, 1.0f, 0);
+    }
+  }
+  static_for<0, 4>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    const uint32_t codes = u4_get(c, J);
+    uint32_t t = 0;
+    if constexpr (F == RAZER_W) {
+      const uint32_t y = codes ^ 0x88888888u;                     // nibble 0 where the code is 0x8
+      const uint32_t nz = ((y & 0x77777777u) + 0x77777777u) | y;  // bit 3: nibble != 0
+      t = (~nz & 0x88888888u) >> 2;                               // 0x2 (+1.0) where the code is 0x8
+    }
+    uint32_t w[4];
+    static_for<0, 4>([&](auto ic) {
+      constexpr int b = decltype(ic)::value;
+      const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, b);
+      float q0 = v[0] * s[J / 2], q1 = v[1] * s[J / 2];
+      if constexpr (F == RAZER_W) {
+        const auto u = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t, 1.0f, b);
+        q0 = __builtin_fmaf(u[0], sp[J / 2], q0);
+        q1 = __builtin_fmaf(u[1], sp[J / 2], q1);
+      }
+      w[b] = __builtin_amdgcn_perm(__float_as_uint(q1), __float_as_uint(q0), 0x07060302u);  // upper halves
+    });
+    out[J] = make_uint4(w[0], w[1], w[2], w[3]);
+  });
+}
+
 // chunks per split: whole windows, as even as that allows
 __host__ __device__ inline int64_t sm_split_len(int64_t nch, int64_t splits, int win) {
   const int64_t q = (nch + splits - 1) / splits;
   return (q + win - 1) / win * win;
 }
 
-template <int FA, int FW, bool OUT_BF16, int MR>
+// A16: the weight-only variant (bf16 activations, p.a_bf16 with pitch p.lda):
+// the activation pieces are copied into the fragments as they are, the
+// weight is decoded to bf16 and the MFMA is the bf16 one; C = RN32(g_w acc).
+template <int FA, int FW, bool OUT_BF16, int MR, bool A16 = false>
 __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm_small_m_kernel(GemmParams p) {
   using C = SmCfg<MR>;
   constexpr int WIN = C::WIN, TURNS = C::TURNS, FPW = C::FPW;
-  __shared__ __align__(16) half8 adec[WIN][MR][4][64];
+  __shared__ __align__(16) uint4 adec[WIN][MR][4][64];
   const int split = (int)(blockIdx.x % (unsigned)p.splits);
   const int64_t slab = blockIdx.x / (unsigned)p.splits;
   // the wave index is uniform: read it into a scalar so that the buffer
@@ -1497,7 +1552,17 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
     const int f = wave + C::WAVES * t;
     pc[t] = f % WIN;
     pb[t] = f / WIN;
-    av[t] = sm_rows(p.a_codes, p.a_scales, min((int64_t)(32 * pb[t]), p.M - 1), p.M, p.K, r32, kh);
+    if constexpr (A16) {
+      // bf16 rows: the lane's half chunk is 32 consecutive elements, 64 bytes
+      const int64_t r0 = min((int64_t)(32 * pb[t]), p.M - 1);
+      const int64_t r = min((int64_t)r32, p.M - 1 - r0);
+      av[t].codes = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_bf16 + r0 * p.lda), (short)0, -1, (int)kRsrcWord3);
+      av[t].scales = av[t].codes;
+      av[t].voff_c = (int)(r * p.lda * 2 + kh * 64);
+      av[t].voff_s = 0;
+    } else {
+      av[t] = sm_rows(p.a_codes, p.a_scales, min((int64_t)(32 * pb[t]), p.M - 1), p.M, p.K, r32, kh);
+    }
   });
   const SmRows wv = sm_rows(p.w_codes, p.w_scales, live ? n0 : p.N - 1, p.N, p.K, r32, kh);
 
@@ -1505,12 +1570,22 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
   static_for<0, MR>([&](auto bc) { acc[decltype(bc)::value] = f32x16{}; });
   // ring: turn J of every window holds its chunks in rc[J] and their scales
   // in sc[J]; per >= WIN, so the first two turns are inside the split
-  uint4 rc[TURNS][kSmRing], sc[TURNS], ca[FPW];
+  uint4 rc[TURNS][kSmRing], sc[TURNS], ca[FPW][A16 ? 4 : 1];
   uint32_t sa[FPW];
-  static_for<0, FPW>([&](auto tc) {
+  // A piece t of the window at chunk base wb: codes and scales, or 64 bytes of bf16
+  auto load_a = [&](auto tc, int64_t wb) {
     constexpr int t = decltype(tc)::value;
-    sm_load_a(av[t], cb + pc[t], ca[t], sa[t]);
-  });
+    if constexpr (A16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ca[t][j] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(av[t].codes, av[t].voff_c,
+                                                                  (int)((wb + pc[t]) * 128 + 16 * j), 0));
+    } else {
+      sm_load_a(av[t], wb + pc[t], ca[t][0], sa[t]);
+    }
+  };
+  const float spw[4] = {p.w_special[0], p.w_special[1], p.w_special[2], p.w_special[3]};
+  static_for<0, FPW>([&](auto tc) { load_a(tc, cb); });
   __builtin_amdgcn_sched_barrier(0);  // A first, then the ring in slot order
   static_for<0, TURNS>([&](auto jc) {
     constexpr int J = decltype(jc)::value;
@@ -1530,10 +1605,7 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
     constexpr bool RF = decltype(refill)::value;
     const int64_t g0 = wb + kSmRing * J;
     if constexpr (decltype(next_a)::value && J == 0) {  // a whole window ahead
-      static_for<0, FPW>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        sm_load_a(av[t], wb + WIN + pc[t], ca[t], sa[t]);
-      });
+      static_for<0, FPW>([&](auto tc) { load_a(tc, wb + WIN); });
       __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t sw[kSmRing];
@@ -1552,8 +1624,16 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
       constexpr int u = decltype(uc)::value;
       // decode the slot, then refill it: the refill's registers are then free
       // and stay the slot's own, with no copies around the loop
-      half8 w[4];
-      if (live) sm_decode<FW>(rc[J][u], sw[u], sp_lo, sp_hi, w);
+      uint4 w[4];
+      if (live) {
+        if constexpr (A16) {
+          sm_decode_bf16<FW>(rc[J][u], sw[u], spw, w);
+        } else {
+          half8 wh[4];
+          sm_decode<FW>(rc[J][u], sw[u], sp_lo, sp_hi, wh);
+          static_for<0, 4>([&](auto ic) { w[decltype(ic)::value] = __builtin_bit_cast(uint4, wh[decltype(ic)::value]); });
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (RF) rc[J][u] = sm_codes(wv, g0 + WIN + u);
       __builtin_amdgcn_sched_barrier(0);
@@ -1562,7 +1642,13 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
           constexpr int I = decltype(ic)::value;
           static_for<0, MR>([&](auto bc) {
             constexpr int b = decltype(bc)::value;
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(adec[kSmRing * J + u][b][I][lane], w[I], acc[b], 0, 0, 0);
+            const uint4 af = adec[kSmRing * J + u][b][I][lane];
+            if constexpr (A16)
+              acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
+                                                               __builtin_bit_cast(bf16x8, w[I]), acc[b], 0, 0, 0);
+            else
+              acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, af),
+                                                              __builtin_bit_cast(half8, w[I]), acc[b], 0, 0, 0);
           });
         });
       }
@@ -1573,12 +1659,19 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
     lds_barrier();  // the previous window's fragments have been read
     static_for<0, FPW>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
-      half8 d[4];
-      sm_decode<FA>(ca[t], sa[t] >> (16 * kh), sp_lo, sp_hi, d);
-      static_for<0, 4>([&](auto ic) {
-        constexpr int I = decltype(ic)::value;
-        adec[pc[t]][pb[t]][I][lane] = d[I];
-      });
+      if constexpr (A16) {
+        static_for<0, 4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          adec[pc[t]][pb[t]][I][lane] = ca[t][I];
+        });
+      } else {
+        half8 d[4];
+        sm_decode<FA>(ca[t][0], sa[t] >> (16 * kh), sp_lo, sp_hi, d);
+        static_for<0, 4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          adec[pc[t]][pb[t]][I][lane] = __builtin_bit_cast(uint4, d[I]);
+        });
+      }
     });
     lds_barrier();
     static_for<0, TURNS>([&](auto jc) {
@@ -1590,7 +1683,8 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
   window(wb, std::true_type{});
   if (!live) return;
 
-  const float gg = (p.a_global ? *p.a_global : 1.0f) * (p.w_global ? *p.w_global : 1.0f);
+  const float gg = A16 ? (p.w_global ? *p.w_global : 1.0f)
+                       : (p.a_global ? *p.a_global : 1.0f) * (p.w_global ? *p.w_global : 1.0f);
   const int64_t col = n0 + r32;
   if (col >= p.N) return;
   static_for<0, MR>([&](auto bc) {
@@ -1641,7 +1735,7 @@ int64_t sm_choose_splits(int64_t M, int64_t N, int64_t nch, int64_t slabs, int64
   return best;
 }
 
-template <int FA, int FW, int MR>
+template <int FA, int FW, int MR, bool A16 = false>
 hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspace& ws) {
   constexpr int WIN = SmCfg<MR>::WIN, WAVES = SmCfg<MR>::WAVES;
   GemmParams p = p0;
@@ -1654,7 +1748,7 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspac
     int per_cu = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
     if (per_cu == 0) {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR>, 64 * WAVES, 0)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR, A16>, 64 * WAVES, 0)
           != hipSuccess || nb < 1)
         nb = 1;
       per_cu = nb;
@@ -1667,19 +1761,19 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspac
   p.splits = (int)sp;
   const unsigned grid = (unsigned)(slabs * sp);
   const unsigned threads = 64 * WAVES;
-  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR>), dim3(grid), dim3(threads), 0, s, p);
-  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR>), dim3(grid), dim3(threads), 0, s, p);
+  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR, A16>), dim3(grid), dim3(threads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR, A16>), dim3(grid), dim3(threads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.splits > 1) e = launch_reduce(p, s);
   return e;
 }
 
-template <int FA, int FW>
+template <int FA, int FW, bool A16 = false>
 hipError_t launch_small_m(const GemmParams& p, hipStream_t s, const Workspace& ws) {
   switch (sm_blocks(p.M)) {
-    case 1: return launch_small_m_mr<FA, FW, 1>(p, s, ws);
-    case 2: return launch_small_m_mr<FA, FW, 2>(p, s, ws);
-    default: return launch_small_m_mr<FA, FW, 4>(p, s, ws);
+    case 1: return launch_small_m_mr<FA, FW, 1, A16>(p, s, ws);
+    case 2: return launch_small_m_mr<FA, FW, 2, A16>(p, s, ws);
+    default: return launch_small_m_mr<FA, FW, 4, A16>(p, s, ws);
   }
 }
 
@@ -1744,6 +1838,25 @@ float* noalloc_scratch() {
     looked_up[dev] = true;
   }
   return (float*)addr[dev];
+}
+
+// Weight-only matmul: the small-M kernel with bf16 activations, 128 rows of A
+// per launch (the weight is streamed once per launch)
+hipError_t launch_gemm_w4a16(int fw, const GemmParams& p0, hipStream_t s, const Workspace& ws) {
+  if (p0.M == 0 || p0.N == 0) return hipSuccess;
+  const int es = p0.c_bf16 ? 2 : 4;
+  for (int64_t m0 = 0; m0 < p0.M; m0 += kSmallM) {
+    GemmParams p = p0;
+    p.partials = nullptr;
+    p.splits = 1;
+    p.M = std::min<int64_t>(kSmallM, p0.M - m0);
+    p.a_bf16 = p0.a_bf16 + m0 * p0.lda;
+    p.c = (uint8_t*)p0.c + m0 * p0.ldc * es;
+    const hipError_t e = fw == RAZER_W ? launch_small_m<NVFP4, RAZER_W, true>(p, s, ws)
+                                       : launch_small_m<NVFP4, NVFP4, true>(p, s, ws);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(int fa, int fw, const GemmParams& p0, hipStream_t s, const Workspace& ws) {

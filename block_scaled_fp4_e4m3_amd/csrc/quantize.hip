@@ -1231,6 +1231,119 @@ int mx32_grid(int64_t rows, int64_t rpr) {
   return (int)std::max(base, want / base * base);
 }
 
+// ---------------------------------------------------------------- RaZeR special-value search
+// RaZeR summary 2.2: the weight table's special values are chosen offline,
+// multiples of 0.5, by quantization error.  The candidate magnitudes are the
+// multiples of 0.5 in (0, 7.5] that are not E2M1 magnitudes; a table is
+// {+a, -a, +b, -b} for a pair a < b (28 pairs, lexicographic).  Every 16-element
+// block (RaZeR-W: abs-max E3M3 scale under g) takes the table's value with the
+// lowest block error, and a table's tensor error is the binary64 sum over
+// rows (ascending) of the binary64 sum over each row's blocks (ascending).
+// One thread per row: it forms the block's error for each of the 16 signed
+// candidates (the block error of RaZeR-W quantization), then, per pair, adds
+// the smallest of its four to the row's 28 sums.
+constexpr int kSearchCand = 8, kSearchPairs = kRazerPairs;
+constexpr float kSearchMag[kSearchCand] = {2.5f, 3.5f, 4.5f, 5.0f, 5.5f, 6.5f, 7.0f, 7.5f};
+
+struct SearchTables {
+  uint32_t elt[64][8];                // per E3M3 code: 7 element thresholds (strict >)
+  uint32_t smid6[64];                 // scale midpoints for T = 6
+  uint32_t lo[64][kSearchCand];       // special interval of each magnitude, strict >
+  uint32_t hi[64][kSearchCand];       // ... strict <
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void razer_search_rows_kernel(QuantParams p, double* row_sums) {
+  __shared__ SearchTables T;
+  const float g = p.global ? *p.global : 1.0f;
+  const double gd = (double)g;
+  for (int k = threadIdx.x; k < 64; k += blockDim.x) {
+    const double sg = sf_val<1>(k) * gd;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) T.elt[k][j] = (k > 0 && j < 7) ? thr_bits(kMidD[j] * sg, (j & 1) != 0) : 0x7F800000u;
+    T.smid6[k] = k < 63 ? thr_bits(0.5 * (sf_val<1>(k) + sf_val<1>(k + 1)) * 6.0 * gd, (k & 1) != 0) : 0xFFFFFFFFu;
+#pragma unroll
+    for (int c = 0; c < kSearchCand; ++c) {
+      float lo, hi;
+      bool open_hi;
+      special_bounds(kSearchMag[c], lo, hi, open_hi);
+      T.lo[k][c] = k == 0 ? 0x7F800000u : thr_bits((double)lo * sg, false);
+      T.hi[k][c] = (k == 0 || open_hi) ? 0x7F800000u : ru_bits((double)hi * sg);
+    }
+  }
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= p.rows) return;  // no barrier follows
+  const double inv6 = 1.0 / (6.0 * gd);
+  double sums[kSearchPairs];
+#pragma unroll
+  for (int q = 0; q < kSearchPairs; ++q) sums[q] = 0.0;
+  for (int64_t b = 0; b < p.cols / 16; ++b) {
+    Raw<16, BF16> raw;
+    load_raw<16, BF16>(p, r, 16 * b, raw);
+    float x[16];
+    finish_chunk<16, BF16, false>(p, 16 * b, raw, x, false, 0);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+    const int k = select_scale<1>(bitsf(amax), T.smid6, inv6);
+    const float s = (float)sf_val<1>(k);
+    uint32_t t[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
+    float err[2 * kSearchCand];
+#pragma unroll
+    for (int c = 0; c < kSearchCand; ++c) {
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const float v = sg ? -kSearchMag[c] : kSearchMag[c];
+        const uint32_t vsign = sg ? 0x80000000u : 0u;
+        const uint32_t p0 = k ? encode_special<8>(x, t, T.lo[k][c], T.hi[k][c], vsign) : 0u;
+        const uint32_t p1 = k ? encode_special<8>(x + 8, t, T.lo[k][c], T.hi[k][c], vsign) : 0u;
+        err[2 * c + sg] = lane_sse<8>(x, p0, s, g, true, v * s) + lane_sse<8>(x + 8, p1, s, g, true, v * s);
+      }
+    }
+    int q = 0;
+#pragma unroll
+    for (int i = 0; i < kSearchCand; ++i)
+#pragma unroll
+      for (int j = i + 1; j < kSearchCand; ++j, ++q) {
+        const float m = fminf(fminf(err[2 * i], err[2 * i + 1]), fminf(err[2 * j], err[2 * j + 1]));
+        sums[q] = sums[q] + (double)m;
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < kSearchPairs; ++q) row_sums[r * kSearchPairs + q] = sums[q];
+}
+
+// per pair, the sum over rows in ascending order; then the smallest (a tie
+// keeps the earlier pair) as the table {+a, -a, +b, -b}
+__global__ void razer_search_reduce_kernel(const double* row_sums, int64_t rows, double* pair_sse, float* table) {
+  __shared__ double tot[kSearchPairs];
+  const int q = threadIdx.x;
+  if (q < kSearchPairs) {
+    double acc = 0.0;
+    for (int64_t r = 0; r < rows; ++r) acc = acc + row_sums[r * kSearchPairs + q];
+    tot[q] = acc;
+    pair_sse[q] = acc;
+  }
+  __syncthreads();
+  if (q == 0) {
+    int best = 0;
+    for (int i = 1; i < kSearchPairs; ++i)
+      if (tot[i] < tot[best]) best = i;
+    int n = 0;
+    for (int i = 0; i < kSearchCand; ++i)
+      for (int j = i + 1; j < kSearchCand; ++j, ++n)
+        if (n == best) {
+          table[0] = kSearchMag[i];
+          table[1] = -kSearchMag[i];
+          table[2] = kSearchMag[j];
+          table[3] = -kSearchMag[j];
+        }
+  }
+}
+
 // ---------------------------------------------------------------- global amax
 __global__ void zero_global_kernel(float* g) { *(uint32_t*)g = 0u; }
 
@@ -1472,6 +1585,30 @@ hipError_t launch_q2(int block, bool bf16, const QuantParams& p, hipStream_t s) 
   }
 }
 
+// automatic global scale of the transformed tensor into *p.global: zero it,
+// the abs-max pass, then g = amax / denom (1 for an all-zero tensor)
+hipError_t launch_auto_global(const QuantParams& p, float denom, hipStream_t s) {
+  const bool bf16 = p.x_bf16 != 0;
+  hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
+  if (p.cols % 8 == 0) {
+    int grid = grid_for(p.rows * (p.cols / 8), 256 * 4);
+    const bool contig = p.ld == p.cols && p.chan_scale == nullptr;
+    if (contig) {
+      if (bf16) hipLaunchKernelGGL((amax_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((amax_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+      if (bf16) hipLaunchKernelGGL((amax_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((amax_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    }
+  } else {
+    int grid = grid_for(p.rows * (p.cols / 4), 256 * 4);
+    if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(amax4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+  }
+  hipLaunchKernelGGL(finalize_global_kernel, dim3(1), dim3(1), 0, s, p.global, denom);
+  return hipGetLastError();
+}
+
 template <int RULE, bool BF16, bool CHAN>
 hipError_t launch_mx_hs(const QuantParams& q, int grid, hipStream_t s) {
   if (q.hadamard == 32) hipLaunchKernelGGL((mx32_kernel<BF16, CHAN, 32, RULE>), dim3(grid), dim3(kThreads), 0, s, q);
@@ -1500,24 +1637,7 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
     // small tensor: one workgroup finds g and quantizes, in one launch
     q.fused_denom = denom;
   } else if (gmode == G_AUTO) {
-    hipLaunchKernelGGL(zero_global_kernel, dim3(1), dim3(1), 0, s, p.global);
-    if (p.cols % 8 == 0) {
-      int grid = grid_for(p.rows * (p.cols / 8), 256 * 4);
-      const bool contig = p.ld == p.cols && p.chan_scale == nullptr;
-      if (contig) {
-        if (bf16) hipLaunchKernelGGL((amax_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((amax_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, p);
-      } else {
-        if (bf16) hipLaunchKernelGGL((amax_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((amax_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, p);
-      }
-    } else {
-      int grid = grid_for(p.rows * (p.cols / 4), 256 * 4);
-      if (bf16) hipLaunchKernelGGL(amax4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL(amax4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
-    }
-    hipLaunchKernelGGL(finalize_global_kernel, dim3(1), dim3(1), 0, s, p.global, denom);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_auto_global(p, denom, s);
     if (e != hipSuccess) return e;
   }
   switch (fmt) {
@@ -1537,6 +1657,22 @@ hipError_t launch_quantize(int fmt, int block, int rule, int gmode, const QuantP
       if (rule == BRUTE) return launch_q2<NVFP4, BRUTE>(block, bf16, q, s);
       return launch_q2<NVFP4, ABSMAX>(block, bf16, q, s);
   }
+}
+
+hipError_t launch_razer_search(const QuantParams& p, int gmode, double* row_sums, double* pair_sse, float* table,
+                               hipStream_t s) {
+  if (gmode == G_AUTO) {
+    const hipError_t e = launch_auto_global(p, 180.0f, s);
+    if (e != hipSuccess) return e;
+  }
+  const unsigned grid = (unsigned)((p.rows + kThreads - 1) / kThreads);
+  if (p.rows > 0) {
+    if (p.x_bf16) hipLaunchKernelGGL(razer_search_rows_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, row_sums);
+    else hipLaunchKernelGGL(razer_search_rows_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, row_sums);
+  }
+  hipLaunchKernelGGL(razer_search_reduce_kernel, dim3(1), dim3(64), 0, s, (const double*)row_sums, p.rows, pair_sse,
+                     table);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequantize(int fmt, int block, const DequantParams& p, hipStream_t s) {

@@ -37,8 +37,9 @@
  *
  * Ownership: the caller allocates and owns every buffer it passes.  The only
  * device memory libfp4q allocates itself is a split-K workspace of 32 MiB per
- * (device, stream), taken with hipMalloc when fp4q_gemm_w4a4 first splits K on
- * that stream and kept until the process ends.  Calls are thread-safe.
+ * (device, stream), taken with hipMalloc when fp4q_gemm_w4a4 or fp4q_gemm_w4a16
+ * first splits K on that stream and kept until the process ends.  Calls are
+ * thread-safe.
  *
  * Asynchrony: every call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t passed as void*, NULL = default stream)
@@ -209,6 +210,29 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
                                    fp4q_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * Weight-only matmul C = g_w * A W^^T with bf16 activations A (M x K, row
+ * pitch lda elements) and a block-16 weight W^ (N x K) in NVFP4 or RAZER_W
+ * (RaZeR summary 2.3: the weight-only kernel next to the weight-activation
+ * one).  The weight decodes exactly to bf16 (value * scale, or the block's
+ * special value * scale at code 0x8); products accumulate in FP32 and
+ * C = RN32(g_w * acc), stored fp32 or bf16 (RNE).  K may be split as in
+ * fp4q_gemm_w4a4, with the same summation rule, determinism and workspace.
+ *   a         device bf16 (uint16 bit patterns), 16-byte aligned, lda % 8 == 0
+ *   fw        NVFP4 or RAZER_W
+ *   w_codes, w_scales  device, as fp4q_quantize writes them (block 16), 16-byte aligned
+ *   w_global  device FP32 or NULL (= 1.0)
+ *   w_special host, 4 floats, required when fw == RAZER_W
+ *   c         device, M x N (pitch ldc elements), 16-byte aligned
+ * Errors: NULL pointer -> ERR_NULL; another format -> ERR_FORMAT; M, N < 0,
+ * K <= 0, K % 512 (the kernel's K window), K > 2^24, lda < K, lda > 2^24 or
+ * ldc < N -> ERR_SHAPE; bad special value -> ERR_ARG; misalignment ->
+ * ERR_ALIGN.  M == 0 or N == 0 enqueues nothing.
+ */
+fp4q_status fp4q_gemm_w4a16(const uint16_t* a, int64_t lda, fp4q_format fw, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* w_global, const float* w_special, int64_t M,
+                            int64_t N, int64_t K, void* c, fp4q_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
  * Per-channel scale of MACaQ's online scaling (MACaQ review, section 3):
  *   t_j = (rms_j(W) / rms_j(X))^alpha, r_j = RN32(1 / t_j),
  * rms over the rows of each column, computed in binary64 and rounded to fp32;
@@ -257,6 +281,37 @@ fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x
 fp4q_status fp4q_macaq_quantize(const float* w, int64_t N, int64_t K, int64_t ldw, const double* h,
                                 int64_t ldh, int64_t max_moves, uint8_t* codes, uint8_t* scales,
                                 int32_t* moves, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Offline choice of RaZeR-W's special values (RaZeR summary 2.2: the weight
+ * table's four values are precomputed offline, multiples of 0.5, by
+ * quantization error).  Candidates are the magnitudes a in {2.5, 3.5, 4.5, 5,
+ * 5.5, 6.5, 7, 7.5} (the multiples of 0.5 up to 7.5 that are not E2M1
+ * magnitudes); a table is {+a, -a, +b, -b} for a pair a < b, 28 pairs in
+ * lexicographic order (a, b) = (2.5, 3.5), (2.5, 4.5), ... (7, 7.5).  Each
+ * 16-element block of w takes RaZeR-W quantization under the global scale
+ * (abs-max E3M3 scale, round-to-nearest codes, the element rule of
+ * fp4q_quantize) with the one signed candidate of the table that gives the
+ * lowest block error (the FP32 error of fp4q_quantize's RaZeR-W).  A pair's
+ * error is the binary64 sum over rows, ascending, of the binary64 sum over
+ * each row's blocks, ascending, of that lowest block error.
+ *   w           device, rows x cols, pitch ld_w (fp32 or bf16), 16-byte aligned
+ *   global_mode NONE (g = 1), AUTO (g = RN32(amax / 180), 1 for an all-zero
+ *               w, written to *global as fp4q_quantize's RAZER_W does),
+ *               GIVEN (*global read)
+ *   pair_sse    device, 28 doubles: each pair's error, written
+ *   table       device, 4 floats: {+a, -a, +b, -b} of the pair with the
+ *               lowest error (a tie keeps the earlier pair), written; pass it
+ *               (copied to the host) as fp4q_quant_desc.special
+ *   workspace   device, 8-byte aligned, at least rows * 28 * 8 bytes
+ * Errors: NULL pointer -> ERR_NULL; rows < 0, cols <= 0, cols % 16 or
+ * ld_w < cols -> ERR_SHAPE; bad dtype or mode, or a small workspace ->
+ * ERR_ARG; misalignment -> ERR_ALIGN.  rows == 0 (w and workspace may then
+ * be NULL) writes zero errors and the first pair.
+ */
+fp4q_status fp4q_razer_table_search(const void* w, fp4q_dtype w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                                    fp4q_global_mode global_mode, float* global, double* pair_sse, float* table,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* fp4q_status_string(fp4q_status s);

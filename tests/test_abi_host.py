@@ -79,6 +79,8 @@ L.fp4q_gemm_w4a4.argtypes = [ci, vp, vp, vp, ci, vp, vp, vp, vp, i64, i64, i64, 
 L.fp4q_gemm_w4a4_noalloc.argtypes = L.fp4q_gemm_w4a4.argtypes
 L.fp4q_channel_scale.argtypes = [vp, ci, i64, i64, vp, ci, i64, i64, i64, ctypes.c_double, vp, vp, vp]
 L.fp4q_macaq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+L.fp4q_gemm_w4a16.argtypes = [vp, i64, ci, vp, vp, vp, vp, i64, i64, i64, vp, ci, i64, vp]
+L.fp4q_razer_table_search.argtypes = [vp, ci, i64, i64, i64, ci, vp, vp, vp, vp, ctypes.c_size_t, vp]
 P = 0x100000  # aligned fake device address; never dereferenced on any error path
 
 def desc(**kw):
@@ -109,6 +111,12 @@ def gn(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc
 
 def mq(w=P, N=4, K=64, ldw=64, h=P, ldh=64, mm=10, codes=P, scales=P, moves=None, ws=P, wsb=1 << 20):
     return L.fp4q_macaq_quantize(w, N, K, ldw, h, ldh, mm, codes, scales, moves, ws, wsb, None)
+
+def wa(a=P, lda=512, fw=0, w=P, sw=P, g=None, sp=None, M=8, N=8, K=512, c=P, ct=0, ldc=8):
+    return L.fp4q_gemm_w4a16(a, lda, fw, w, sw, g, sp, M, N, K, c, ct, ldc, None)
+
+def ts(w=P, wt=0, rows=4, cols=64, ld=64, gmode=1, g=P, sse=P, table=P, ws=P, wsb=1 << 20):
+    return L.fp4q_razer_table_search(w, wt, rows, cols, ld, gmode, g, sse, table, ws, wsb, None)
 
 def cs(x=P, rows_x=4, ldx=8, w=P, rows_w=4, ldw=8, cols=8, alpha=0.75, t=P, r=P):
     return L.fp4q_channel_scale(x, 0, rows_x, ldx, w, 0, rows_w, ldw, cols, alpha, t, r, None)
@@ -158,6 +166,15 @@ res = {
  # MACaQ calibration
  "m_null_w": mq(w=None), "m_null_ws": mq(ws=None), "m_K": mq(K=48, ldw=64), "m_K_big": mq(K=5152, ldw=5152, ldh=5152),
  "m_ldh": mq(ldh=32), "m_N": mq(N=-1), "m_moves": mq(mm=-1), "m_ws": mq(wsb=8 * 64 - 8), "m_align": mq(h=P + 4),
+ # weight-only matmul
+ "w_null_a": wa(a=None), "w_null_sp": wa(fw=3), "w_format_mx": wa(fw=1), "w_format_ra": wa(fw=2),
+ "w_K": wa(K=256, lda=256), "w_lda": wa(lda=256), "w_lda_big": wa(lda=(1 << 24) + 8), "w_ldc": wa(ldc=4),
+ "w_M": wa(M=-1), "w_align_a": wa(a=P + 8), "w_align_lda": wa(lda=516), "w_align_sw": wa(sw=P + 4),
+ "w_dtype": wa(ct=2), "w_special": wa(fw=3, sp=ctypes.cast((ctypes.c_float * 4)(5.0, -5.0, 4.0, -2.5), vp)),
+ # special-value search
+ "t_null_w": ts(w=None), "t_null_w0": ts(w=None, rows=0, ws=None, gmode=5), "t_null_table": ts(table=None), "t_null_g": ts(g=None), "t_null_ws": ts(ws=None),
+ "t_cols": ts(cols=40, ld=40), "t_ld": ts(ld=32), "t_rows": ts(rows=-1), "t_ws": ts(wsb=4 * 28 * 8 - 8),
+ "t_mode": ts(gmode=3), "t_dtype": ts(wt=4), "t_align": ts(sse=P + 4), "t_align_w": ts(ld=66),
  # channel scale
  "c_null": cs(t=None), "c_rows": cs(rows_x=0), "c_ld": cs(ldx=4), "c_alpha": cs(alpha=float("inf")),
 }
@@ -183,6 +200,10 @@ EXPECTED = {
     "gn_null_a": 1, "gn_mixed": 4, "gn_K_block": 2, "gn_align": 3, "gn_dtype": 5,
     "m_null_w": 1, "m_null_ws": 1, "m_K": 2, "m_K_big": 2, "m_ldh": 2, "m_N": 2, "m_moves": 5, "m_ws": 5,
     "m_align": 3,
+    "w_null_a": 1, "w_null_sp": 1, "w_format_mx": 4, "w_format_ra": 4, "w_K": 2, "w_lda": 2, "w_lda_big": 2,
+    "w_ldc": 2, "w_M": 2, "w_align_a": 3, "w_align_lda": 3, "w_align_sw": 3, "w_dtype": 5, "w_special": 5,
+    "t_null_w": 1, "t_null_w0": 5, "t_null_table": 1, "t_null_g": 1, "t_null_ws": 1, "t_cols": 2, "t_ld": 2, "t_rows": 2,
+    "t_ws": 5, "t_mode": 5, "t_dtype": 5, "t_align": 3, "t_align_w": 3,
     "c_null": 1, "c_rows": 2, "c_ld": 2, "c_alpha": 5,
 }
 
@@ -202,8 +223,9 @@ def test_zero_rows_and_empty_gemm_enqueue_nothing():
     # with no visible device
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     code = f"ROOT = {ROOT!r}\nLIB = {LIB!r}\n" + CHILD.split("res = {")[0] + textwrap.dedent('''
-print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0), mq(N=0))
+print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0), mq(N=0), wa(M=0),
+      wa(N=0))
 ''')
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == ["0"] * 7
+    assert out.stdout.split() == ["0"] * 9

@@ -338,11 +338,11 @@ def test_prefill_workload(B, N):
     check(got, ref, "bf16" if N == 17408 else "f32")
 
 
-# FP32 output on launches with few tiles splits K in two halves that add with
-# FP32 atomics; the sum of two halves does not depend on which lands first, so
-# repeated launches give the same bytes: the decode workload at M = 128
-# (small-M kernel) and a two-tile shape of the tile kernel, both formats.
-# Parity at these shapes is the business of the workload and staging tests.
+# Launches with few output tiles split K; the splits' partial results are
+# added by a separate pass in split order, so repeated launches give the same
+# bytes: the decode workload at M = 16 and 128 (small-M kernel) and two-tile
+# shapes of the tile kernel, both formats.  Parity at these shapes is the
+# business of the workload and staging tests.
 @pytest.mark.parametrize("fa,fw,M,N,K", [("razer_a", "razer_w", 128, 17408, 5120), ("nvfp4", "nvfp4", 200, 300, 1024),
                                          ("mxfp4", "mxfp4", 200, 300, 2048), ("nvfp4", "nvfp4", 16, 17408, 5120)])
 def test_gemm_fp32_split_k_is_deterministic(B, fa, fw, M, N, K):
