@@ -63,6 +63,10 @@ _SIGS = {
                                       _i64, _vp]),
     "fp4q_channel_scale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp]),
     "fp4q_macaq_quantize": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "fp4q_gemm_w4a4_segmented": (_int, [_int, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64,
+                                        _vp, _int, _i64, _vp]),
+    "fp4q_gemm_w4a4_act_bf16": (_int, [_vp, _i64, _u32, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _int, _vp, _i64,
+                                       _i64, _i64, _vp, _int, _i64, _vp]),
     "fp4q_gemm_w4a16": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _i64, _vp]),
     "fp4q_razer_table_search": (_int, [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                        _vp]),
@@ -199,6 +203,40 @@ def fp4q_macaq_quantize(w, N: int, K: int, ldw: int, h, ldh: int, max_moves: int
            "fp4q_macaq_quantize")
 
 
+def _seg(seg_rows):
+    if seg_rows is None or len(seg_rows) == 0:
+        return None, 0
+    arr = (ctypes.c_int64 * len(seg_rows))(*[int(v) for v in seg_rows])
+    return arr, len(seg_rows)
+
+
+def _special_arr(w_special):
+    return None if w_special is None else (ctypes.c_float * 4)(*[float(v) for v in w_special])
+
+
+def fp4q_gemm_w4a4_segmented(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_global, seg_rows,
+                             w_special, M: int, N: int, K: int, c, c_dtype: int, ldc: int, stream=None) -> None:
+    seg, nseg = _seg(seg_rows)
+    sp = _special_arr(w_special)
+    _check(_lib.fp4q_gemm_w4a4_segmented(_fmt(fa), _ptr(a_codes), _ptr(a_scales), _ptr(a_global), _fmt(fw),
+                                         _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                         ctypes.cast(seg, ctypes.c_void_p) if seg is not None else None, nseg,
+                                         ctypes.cast(sp, ctypes.c_void_p) if sp is not None else None,
+                                         M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a4_segmented")
+
+
+def fp4q_gemm_w4a4_act_bf16(a, lda: int, a_rule, a_global, a_codes_out, a_scales_out, fw, w_codes, w_scales,
+                            w_global, seg_rows, w_special, M: int, N: int, K: int, c, c_dtype: int, ldc: int,
+                            stream=None) -> None:
+    seg, nseg = _seg(seg_rows)
+    sp = _special_arr(w_special)
+    _check(_lib.fp4q_gemm_w4a4_act_bf16(_ptr(a), lda, _rule(a_rule), _ptr(a_global), _ptr(a_codes_out),
+                                        _ptr(a_scales_out), _fmt(fw), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                        ctypes.cast(seg, ctypes.c_void_p) if seg is not None else None, nseg,
+                                        ctypes.cast(sp, ctypes.c_void_p) if sp is not None else None,
+                                        M, N, K, _ptr(c), c_dtype, ldc, _stream(stream)), "fp4q_gemm_w4a4_act_bf16")
+
+
 def fp4q_gemm_w4a16(a, lda: int, fw, w_codes, w_scales, w_global, w_special, M: int, N: int, K: int, c,
                     c_dtype: int, ldc: int, stream=None) -> None:
     sp = None
@@ -322,3 +360,37 @@ def razer_table_search(w, global_mode="auto", global_=None, stream=None):
     fp4q_razer_table_search(w, _dtype_code(w), rows, cols, w.stride(0), global_mode, global_, pair_sse, table, ws,
                             ws.numel() * 8, stream)
     return table, pair_sse, global_
+
+
+def gemm_segmented(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_globals, seg_rows, w_special=None,
+                   out_dtype=None, out=None, stream=None):
+    """C = A^ W^T with W^ the concatenation of len(seg_rows) weights, segment
+    i taking the global scale w_globals[i] (device fp32 [nseg])."""
+    import torch
+    M, N, K = a_codes.shape[0], w_codes.shape[0], 2 * a_codes.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a_codes.device)
+    fp4q_gemm_w4a4_segmented(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, w_globals, seg_rows, w_special,
+                             M, N, K, out, _dtype_code(out), out.stride(0), stream)
+    return out
+
+
+def gemm_act_bf16(a, rule, a_global, fw, w_codes, w_scales, w_global=None, seg_rows=None, w_special=None,
+                  out_dtype=None, out=None, keep_codes=False, stream=None):
+    """W4A4 matmul of bf16 activations A [M, K] quantized on load (NVFP4,
+    block 16, rule "absmax" or "4over6", global a_global or 1).  Returns C, or
+    (C, codes, scales) with keep_codes."""
+    import torch
+    if a.dtype != torch.bfloat16 or a.stride(1) != 1:
+        raise ValueError("a must be bf16 with unit stride along its last dimension")
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    codes = scales = None
+    if keep_codes:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=a.device)
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=a.device)
+    fp4q_gemm_w4a4_act_bf16(a, a.stride(0), rule, a_global, codes, scales, fw, w_codes, w_scales, w_global, seg_rows,
+                            w_special, M, N, K, out, _dtype_code(out), out.stride(0), stream)
+    return (out, codes, scales) if keep_codes else out

@@ -48,8 +48,8 @@ def _stale(src: str) -> bool:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     if not os.path.exists(obj):
         return True
-    deps = [os.path.join(CSRC, src), os.path.join(CSRC, "fp4q_internal.hpp"),
-            os.path.join(os.path.dirname(PKG), "include", "fp4q.h")]
+    deps = [os.path.join(CSRC, src), os.path.join(os.path.dirname(PKG), "include", "fp4q.h")]
+    deps += [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".hpp")]
     return any(os.path.getmtime(d) > os.path.getmtime(obj) for d in deps)
 
 

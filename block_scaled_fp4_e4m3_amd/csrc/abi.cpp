@@ -113,6 +113,27 @@ fp4q_status gemm_params(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a
   return FP4Q_OK;
 }
 
+// W row segments: nseg == 0 keeps the single w_global; 1..8 segments of
+// seg_rows[i] >= 0 rows summing to N take w_global[i] each
+fp4q_status segment_params(const float* w_global, const int64_t* seg_rows, int nseg, int64_t N, GemmParams& p) {
+  p.nseg = 0;
+  p.seg_global = nullptr;
+  if (nseg == 0) return FP4Q_OK;
+  if (nseg < 0 || nseg > kMaxSegments) return FP4Q_ERR_ARG;
+  if (!seg_rows || !w_global) return FP4Q_ERR_NULL;
+  int64_t end = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (seg_rows[i] < 0 || seg_rows[i] > N - end) return FP4Q_ERR_SHAPE;
+    end += seg_rows[i];
+    p.seg_end[i] = end;
+  }
+  if (end != N) return FP4Q_ERR_SHAPE;
+  for (int i = nseg; i < kMaxSegments; ++i) p.seg_end[i] = N;
+  p.nseg = nseg;
+  p.seg_global = w_global;
+  return FP4Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,6 +219,66 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
   float* scratch = noalloc_scratch();
   if (!scratch) return FP4Q_ERR_DEVICE;
   return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{scratch, kSplitWorkspaceBytes}));
+}
+
+fp4q_status fp4q_gemm_w4a4_segmented(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* a_global, fp4q_format fw, const uint8_t* w_codes,
+                                     const uint8_t* w_scales, const float* w_global, const int64_t* seg_rows,
+                                     int nseg, const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
+                                     fp4q_dtype c_dtype, int64_t ldc, void* stream) {
+  GemmParams p{};
+  fp4q_status st = gemm_params(fa, a_codes, a_scales, a_global, fw, w_codes, w_scales, nullptr, w_special, M, N,
+                               K, c, c_dtype, ldc, p);
+  if (st != FP4Q_OK) return st;
+  if (nseg == 0) p.w_global = w_global;
+  if ((st = segment_params(w_global, seg_rows, nseg, N, p)) != FP4Q_OK) return st;
+  if (w_global && ((uintptr_t)w_global & 3u)) return FP4Q_ERR_ALIGN;
+  if (M == 0 || N == 0) return FP4Q_OK;
+  return device_status(launch_gemm(fa, fw, p, (hipStream_t)stream, Workspace{nullptr, kSplitWorkspaceBytes}));
+}
+
+fp4q_status fp4q_gemm_w4a4_act_bf16(const uint16_t* a, int64_t lda, uint32_t a_rule, const float* a_global,
+                                    uint8_t* a_codes_out, uint8_t* a_scales_out, fp4q_format fw,
+                                    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                    const int64_t* seg_rows, int nseg, const float* w_special, int64_t M,
+                                    int64_t N, int64_t K, void* c, fp4q_dtype c_dtype, int64_t ldc, void* stream) {
+  if (fw != FP4Q_NVFP4 && fw != FP4Q_NVFP4_RAZER_A && fw != FP4Q_NVFP4_RAZER_W) return FP4Q_ERR_FORMAT;
+  if (a_rule != FP4Q_RULE_ABSMAX && a_rule != FP4Q_RULE_4OVER6) return FP4Q_ERR_ARG;
+  if (c_dtype != FP4Q_F32 && c_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (!a || !w_codes || !w_scales || !c) return FP4Q_ERR_NULL;
+  if ((a_codes_out == nullptr) != (a_scales_out == nullptr)) return FP4Q_ERR_NULL;
+  if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
+  if (M < 0 || N < 0 || K <= 0 || K % 512 != 0 || K > (int64_t(1) << 24) || lda < K || lda > (int64_t(1) << 24) ||
+      ldc < N)
+    return FP4Q_ERR_SHAPE;
+  if (fw == FP4Q_NVFP4_RAZER_W)
+    for (int i = 0; i < 4; ++i)
+      if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
+  GemmParams p{};
+  fp4q_status st = segment_params(w_global, seg_rows, nseg, N, p);
+  if (st != FP4Q_OK) return st;
+  if (!aligned16(a) || lda % 8 != 0 || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(c) ||
+      !aligned16(a_codes_out) || !aligned16(a_scales_out) || (ldc * (int64_t)elem_size(c_dtype)) % 16 != 0)
+    return FP4Q_ERR_ALIGN;
+  if ((a_global && ((uintptr_t)a_global & 3u)) || (w_global && ((uintptr_t)w_global & 3u))) return FP4Q_ERR_ALIGN;
+  if (M == 0 || N == 0) return FP4Q_OK;
+  p.a_bf16 = a;
+  p.lda = lda;
+  p.a_global = a_global;
+  p.aq_codes = a_codes_out;
+  p.aq_scales = a_scales_out;
+  p.w_codes = w_codes;
+  p.w_scales = w_scales;
+  p.w_global = nseg == 0 ? w_global : nullptr;
+  for (int i = 0; i < 4; ++i) p.w_special[i] = (fw == FP4Q_NVFP4_RAZER_W) ? w_special[i] : 0.0f;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  p.c_bf16 = c_dtype == FP4Q_BF16;
+  return device_status(launch_gemm_act_bf16(a_rule == FP4Q_RULE_4OVER6 ? FOUR6 : ABSMAX, fw, p, (hipStream_t)stream,
+                                            Workspace{nullptr, kSplitWorkspaceBytes}));
 }
 
 fp4q_status fp4q_gemm_w4a16(const uint16_t* a, int64_t lda, fp4q_format fw, const uint8_t* w_codes,

@@ -42,10 +42,18 @@ struct GemmParams {
   float w_special[4];
   int64_t M, N, K;
   void* c; int64_t ldc; int c_bf16;
-  const uint16_t* a_bf16; int64_t lda;  // weight-only matmul: bf16 activations (M x K, pitch lda)
+  const uint16_t* a_bf16; int64_t lda;  // bf16 activations (M x K, pitch lda): weight-only, or quantized on load
+  uint8_t* aq_codes; uint8_t* aq_scales;  // quantized on load: the activations' codes and scales, or nullptr
+  // W row segments with their own global scales: segment i covers the
+  // output columns [seg_end[i-1], seg_end[i]) (seg_end[-1] = 0) and takes
+  // seg_global[i] in place of w_global; nseg = 0: w_global everywhere
+  int nseg;
+  const float* seg_global;
+  int64_t seg_end[8];
   int splits;       // K-splits per output tile (set by the launcher)
   float* partials;  // splits > 1: the splits' RN32(g * acc_s), dense M x N slices, added in split order
 };
+constexpr int kMaxSegments = 8;
 
 // bytes of the split-K workspace a matmul may use (per stream, or the
 // library's own array for the non-allocating entry point)
@@ -81,6 +89,10 @@ hipError_t launch_gemm(int fa, int fw, const GemmParams& p, hipStream_t s, const
 // weight-only matmul (bf16 activations in p.a_bf16), fw NVFP4 or RAZER_W;
 // needs K % 512 == 0 and 16-byte aligned rows
 hipError_t launch_gemm_w4a16(int fw, const GemmParams& p, hipStream_t s, const Workspace& ws);
+// W4A4 matmul whose NVFP4 activations are quantized from bf16 (p.a_bf16) as
+// they are loaded, rule ABSMAX or FOUR6 under *p.a_global (or 1); fw of the
+// NVFP4 family; needs K % 512 == 0 and 16-byte aligned rows
+hipError_t launch_gemm_act_bf16(int rule, int fw, const GemmParams& p, hipStream_t s, const Workspace& ws);
 // the split-K workspace of stream s on the current device (allocated on first
 // use, kept until the process ends), or nullptr
 float* split_workspace(hipStream_t s);

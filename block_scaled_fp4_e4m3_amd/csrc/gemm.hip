@@ -37,6 +37,7 @@
 // (row, h) owns elements [32h, 32h + 32) of the chunk and MFMA j of the chunk
 // takes its elements [8j, 8j + 8).
 #include "fp4q_internal.hpp"
+#include "nv_encode.hpp"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,6 +59,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256;   // workgroup tile
+
+// global scale of output column col: the segment's, or w_global
+__device__ __forceinline__ float col_w_global(const GemmParams& p, float gw, int64_t col) {
+  if (p.nseg == 0) return gw;
+  int sidx = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSegments - 1; ++i) sidx += (i < p.nseg - 1 && col >= p.seg_end[i]) ? 1 : 0;
+  return p.seg_global[sidx];
+}
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;          // tile rows per group in the tile order
 constexpr int BK = 128;             // K elements per stage
@@ -1220,9 +1230,11 @@ void gemm_tile_kernel(GemmParams p) {
 
   const float ga = p.a_global ? *p.a_global : 1.0f;
   const float gw = p.w_global ? *p.w_global : 1.0f;
-  const float gg = ga * gw;
   const int r32 = lane & 31, kh = lane >> 5;
   const int64_t row0 = m0 + wm * 128, col0 = n0 + wn * 128;
+  float gg[4];  // the lane's four columns col0 + 32 j + r32
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gg[j] = ga * col_w_global(p, gw, col0 + 32 * j + r32);
   const bool inside = row0 + 128 <= p.M && col0 + 128 <= p.N;
   constexpr int ES = OUT_BF16 ? 2 : 4;  // output element bytes
   const int64_t pitch = p.ldc * ES;
@@ -1246,7 +1258,7 @@ void gemm_tile_kernel(GemmParams p) {
         const int soff = (32 * i + (r / 4) * 8 + (r % 4)) * ld;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = gg * acc[i][j][r];
+          const float v = gg[j] * acc[i][j][r];
           if constexpr (OUT_BF16) {
             uint32_t u = __float_as_uint(v);
             u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
@@ -1267,7 +1279,7 @@ void gemm_tile_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = row0 + 32 * i + (r / 4) * 8 + kh * 4 + (r % 4);
         if (!inside && (row >= p.M || col >= p.N)) continue;
-        const float v = gg * acc[i][j][r];
+        const float v = gg[j] * acc[i][j][r];
         if (p.splits > 1) {
           // this split's RN32(g * acc) into its own dense M x N slice
           p.partials[(split * p.M + row) * p.N + col] = v;
@@ -1523,11 +1535,75 @@ __host__ __device__ inline int64_t sm_split_len(int64_t nch, int64_t splits, int
   return (q + win - 1) / win * win;
 }
 
-// A16: the weight-only variant (bf16 activations, p.a_bf16 with pitch p.lda):
-// the activation pieces are copied into the fragments as they are, the
-// weight is decoded to bf16 and the MFMA is the bf16 one; C = RN32(g_w acc).
-template <int FA, int FW, bool OUT_BF16, int MR, bool A16 = false>
-__global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm_small_m_kernel(GemmParams p) {
+// Where the A rows come from.  AM_BF16: the weight-only variant (bf16
+// activations, p.a_bf16 with pitch p.lda): the activation pieces are copied
+// into the fragments as they are, the weight is decoded to bf16 and the MFMA
+// is the bf16 one; C = RN32(g_w acc).  AM_Q_*: bf16 activations quantized to
+// NVFP4 as they are loaded (abs-max or 4-over-6 under g_a), with the
+// quantizer's exact decisions, then decoded as packed A would be: the same
+// fragments, so the result is that of quantizing first and multiplying the
+// codes.  The workgroups of the first column slab also store the codes and
+// scales when p.aq_codes is set.
+enum AMode : int { AM_CODES = 0, AM_BF16 = 1, AM_Q_ABSMAX = 2, AM_Q_FOUR6 = 3 };
+
+// NVFP4 quantization of one 16-element block held by one lane (the block
+// rule of the 16-element-per-lane quantizer): abs-max E4M3 scale by the
+// bracketed hardware convert and one exact midpoint test, codes by the
+// bracketed FP4 convert, 4-over-6 by the FP32 block errors (ties keep 6)
+struct ActQuant {
+  float g, lo6, lo4;
+  double inv6, inv4;
+  bool fast;
+};
+__device__ __forceinline__ ActQuant act_quant_setup(float g) {
+  ActQuant q;
+  q.g = g;
+  q.fast = g > 0x1p-100f && g < 0x1p100f;
+  q.lo6 = __builtin_amdgcn_rcpf(6.0f * g) * (1.0f - 0x1p-20f);
+  q.lo4 = __builtin_amdgcn_rcpf(4.0f * g) * (1.0f - 0x1p-20f);
+  q.inv6 = 1.0 / (6.0 * (double)g);
+  q.inv4 = 1.0 / (4.0 * (double)g);
+  return q;
+}
+template <bool FOUR_OVER_SIX>
+__device__ __forceinline__ void act_quant16(const float* x, const ActQuant& q, uint2& packed, int& sbyte) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+  const bool finite = amax < 0x7F800000u;
+  int k6 = 0, k4 = 0;
+  if (wave_all(q.fast && finite)) {
+    typedef short s2v __attribute__((ext_vector_type(2)));
+    const float a = bitsf(amax);
+    const s2v z = {0, 0};
+    const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * q.lo6, a * q.lo4, 1.0f, false);
+    const uint32_t wl = (uint16_t)clo[0];
+    k6 = e4m3_from_low(wl & 0xFFu, a, 6.0f, q.g);
+    if constexpr (FOUR_OVER_SIX) k4 = e4m3_from_low(wl >> 8, a, 4.0f, q.g);
+  } else {
+    k6 = select_sf_exact<0>(bitsf(amax), q.inv6, 6.0 * (double)q.g);
+    if constexpr (FOUR_OVER_SIX) k4 = select_sf_exact<0>(bitsf(amax), q.inv4, 4.0 * (double)q.g);
+  }
+  const float s6 = sf_f32<0>(k6);
+  packed = encode_nv16<1, 0>(x, k6, s6, q.g, finite);
+  sbyte = k6;
+  if constexpr (FOUR_OVER_SIX) {
+    const float s4 = sf_f32<0>(k4);
+    const uint2 pk4 = encode_nv16<1, 0>(x, k4, s4, q.g, finite);
+    const float e6 = lane_sse16(x, packed, s6, q.g);
+    const float e4 = lane_sse16(x, pk4, s4, q.g);
+    if (e4 < e6) { packed = pk4; sbyte = k4; }
+  }
+  packed.x = clear_neg_zero(packed.x);
+  packed.y = clear_neg_zero(packed.y);
+}
+
+template <int FA, int FW, bool OUT_BF16, int MR, int AM = AM_CODES>
+__global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? (AM >= AM_Q_ABSMAX ? 2 : 4) : 1)) void gemm_small_m_kernel(
+    GemmParams p) {
+  constexpr bool A16 = AM != AM_CODES;      // bf16 rows of A
+  constexpr bool ABF = AM == AM_BF16;       // ... fed to the bf16 MFMA as they are
+  constexpr bool AQ = AM >= AM_Q_ABSMAX;    // ... quantized on load
   using C = SmCfg<MR>;
   constexpr int WIN = C::WIN, TURNS = C::TURNS, FPW = C::FPW;
   __shared__ __align__(16) uint4 adec[WIN][MR][4][64];
@@ -1565,6 +1641,9 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
     }
   });
   const SmRows wv = sm_rows(p.w_codes, p.w_scales, live ? n0 : p.N - 1, p.N, p.K, r32, kh);
+  ActQuant aq{};
+  if constexpr (AQ) aq = act_quant_setup(p.a_global ? *p.a_global : 1.0f);
+  const bool aq_store = AQ && p.aq_codes != nullptr && slab == 0;
 
   f32x16 acc[MR];
   static_for<0, MR>([&](auto bc) { acc[decltype(bc)::value] = f32x16{}; });
@@ -1626,7 +1705,7 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
       // and stay the slot's own, with no copies around the loop
       uint4 w[4];
       if (live) {
-        if constexpr (A16) {
+        if constexpr (ABF) {
           sm_decode_bf16<FW>(rc[J][u], sw[u], spw, w);
         } else {
           half8 wh[4];
@@ -1643,7 +1722,7 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
           static_for<0, MR>([&](auto bc) {
             constexpr int b = decltype(bc)::value;
             const uint4 af = adec[kSmRing * J + u][b][I][lane];
-            if constexpr (A16)
+            if constexpr (ABF)
               acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
                                                                __builtin_bit_cast(bf16x8, w[I]), acc[b], 0, 0, 0);
             else
@@ -1659,7 +1738,45 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
     lds_barrier();  // the previous window's fragments have been read
     static_for<0, FPW>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
-      if constexpr (A16) {
+      if constexpr (AQ) {
+        // the lane's two 16-element blocks: words 0-3 and 4-7 of the 32 bf16
+        uint4 cq;
+        uint32_t sq;
+        {
+          float x[16];
+          uint2 pk[2];
+          int sb[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const uint4 v = ca[t][2 * h + j];
+              const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                x[8 * j + 2 * i] = bitsf(wv4[i] << 16);
+                x[8 * j + 2 * i + 1] = bitsf(wv4[i] & 0xFFFF0000u);
+              }
+            }
+            act_quant16<AM == AM_Q_FOUR6>(x, aq, pk[h], sb[h]);
+          }
+          cq = make_uint4(pk[0].x, pk[0].y, pk[1].x, pk[1].y);
+          sq = (uint32_t)sb[0] | ((uint32_t)sb[1] << 8);
+        }
+        if (aq_store) {
+          const int64_t row = 32 * (int64_t)pb[t] + r32, kc = wb + pc[t];
+          if (row < p.M) {
+            *(uint4*)(p.aq_codes + row * (p.K / 2) + kc * 32 + kh * 16) = cq;
+            *(uint16_t*)(p.aq_scales + row * (p.K / 16) + kc * 4 + kh * 2) = (uint16_t)sq;
+          }
+        }
+        half8 d[4];
+        sm_decode<NVFP4>(cq, sq, 0u, 0u, d);
+        static_for<0, 4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          adec[pc[t]][pb[t]][I][lane] = __builtin_bit_cast(uint4, d[I]);
+        });
+      } else if constexpr (A16) {
         static_for<0, 4>([&](auto ic) {
           constexpr int I = decltype(ic)::value;
           adec[pc[t]][pb[t]][I][lane] = ca[t][I];
@@ -1683,10 +1800,10 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? 4 : 1)) void gemm
   window(wb, std::true_type{});
   if (!live) return;
 
-  const float gg = A16 ? (p.w_global ? *p.w_global : 1.0f)
-                       : (p.a_global ? *p.a_global : 1.0f) * (p.w_global ? *p.w_global : 1.0f);
   const int64_t col = n0 + r32;
   if (col >= p.N) return;
+  const float gw = col_w_global(p, p.w_global ? *p.w_global : 1.0f, col);
+  const float gg = ABF ? gw : (p.a_global ? *p.a_global : 1.0f) * gw;
   static_for<0, MR>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
@@ -1735,7 +1852,7 @@ int64_t sm_choose_splits(int64_t M, int64_t N, int64_t nch, int64_t slabs, int64
   return best;
 }
 
-template <int FA, int FW, int MR, bool A16 = false>
+template <int FA, int FW, int MR, int AM = AM_CODES>
 hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspace& ws) {
   constexpr int WIN = SmCfg<MR>::WIN, WAVES = SmCfg<MR>::WAVES;
   GemmParams p = p0;
@@ -1748,7 +1865,7 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspac
     int per_cu = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
     if (per_cu == 0) {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR, A16>, 64 * WAVES, 0)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_small_m_kernel<FA, FW, false, MR, AM>, 64 * WAVES, 0)
           != hipSuccess || nb < 1)
         nb = 1;
       per_cu = nb;
@@ -1761,19 +1878,19 @@ hipError_t launch_small_m_mr(const GemmParams& p0, hipStream_t s, const Workspac
   p.splits = (int)sp;
   const unsigned grid = (unsigned)(slabs * sp);
   const unsigned threads = 64 * WAVES;
-  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR, A16>), dim3(grid), dim3(threads), 0, s, p);
-  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR, A16>), dim3(grid), dim3(threads), 0, s, p);
+  if (p.c_bf16) hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, true, MR, AM>), dim3(grid), dim3(threads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_small_m_kernel<FA, FW, false, MR, AM>), dim3(grid), dim3(threads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.splits > 1) e = launch_reduce(p, s);
   return e;
 }
 
-template <int FA, int FW, bool A16 = false>
+template <int FA, int FW, int AM = AM_CODES>
 hipError_t launch_small_m(const GemmParams& p, hipStream_t s, const Workspace& ws) {
   switch (sm_blocks(p.M)) {
-    case 1: return launch_small_m_mr<FA, FW, 1, A16>(p, s, ws);
-    case 2: return launch_small_m_mr<FA, FW, 2, A16>(p, s, ws);
-    default: return launch_small_m_mr<FA, FW, 4, A16>(p, s, ws);
+    case 1: return launch_small_m_mr<FA, FW, 1, AM>(p, s, ws);
+    case 2: return launch_small_m_mr<FA, FW, 2, AM>(p, s, ws);
+    default: return launch_small_m_mr<FA, FW, 4, AM>(p, s, ws);
   }
 }
 
@@ -1852,8 +1969,40 @@ hipError_t launch_gemm_w4a16(int fw, const GemmParams& p0, hipStream_t s, const 
     p.M = std::min<int64_t>(kSmallM, p0.M - m0);
     p.a_bf16 = p0.a_bf16 + m0 * p0.lda;
     p.c = (uint8_t*)p0.c + m0 * p0.ldc * es;
-    const hipError_t e = fw == RAZER_W ? launch_small_m<NVFP4, RAZER_W, true>(p, s, ws)
-                                       : launch_small_m<NVFP4, NVFP4, true>(p, s, ws);
+    const hipError_t e = fw == RAZER_W ? launch_small_m<NVFP4, RAZER_W, AM_BF16>(p, s, ws)
+                                       : launch_small_m<NVFP4, NVFP4, AM_BF16>(p, s, ws);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// W4A4 with activations quantized on load: the small-M kernel, 128 rows of A
+// per launch (each launch streams the weight once)
+template <int AM>
+hipError_t launch_act_bf16_fw(int fw, const GemmParams& p, hipStream_t s, const Workspace& ws) {
+  switch (fw) {
+    case RAZER_A: return launch_small_m<NVFP4, RAZER_A, AM>(p, s, ws);
+    case RAZER_W: return launch_small_m<NVFP4, RAZER_W, AM>(p, s, ws);
+    default: return launch_small_m<NVFP4, NVFP4, AM>(p, s, ws);
+  }
+}
+
+hipError_t launch_gemm_act_bf16(int rule, int fw, const GemmParams& p0, hipStream_t s, const Workspace& ws) {
+  if (p0.M == 0 || p0.N == 0) return hipSuccess;
+  const int es = p0.c_bf16 ? 2 : 4;
+  for (int64_t m0 = 0; m0 < p0.M; m0 += kSmallM) {
+    GemmParams p = p0;
+    p.partials = nullptr;
+    p.splits = 1;
+    p.M = std::min<int64_t>(kSmallM, p0.M - m0);
+    p.a_bf16 = p0.a_bf16 + m0 * p0.lda;
+    p.c = (uint8_t*)p0.c + m0 * p0.ldc * es;
+    if (p0.aq_codes) {
+      p.aq_codes = p0.aq_codes + m0 * (p0.K / 2);
+      p.aq_scales = p0.aq_scales + m0 * (p0.K / 16);
+    }
+    const hipError_t e = rule == FOUR6 ? launch_act_bf16_fw<AM_Q_FOUR6>(fw, p, s, ws)
+                                       : launch_act_bf16_fw<AM_Q_ABSMAX>(fw, p, s, ws);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

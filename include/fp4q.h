@@ -210,6 +210,61 @@ fp4q_status fp4q_gemm_w4a4_noalloc(fp4q_format fa, const uint8_t* a_codes, const
                                    fp4q_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * fp4q_gemm_w4a4 for fused projections: W^ is the row-wise concatenation of
+ * nseg weights (say Q, K and V), each quantized under its own global scale.
+ * Segment i holds the seg_rows[i] rows after those of segments 0 .. i-1 and
+ * its output columns take w_global[i]: C[m][n] = RN32(RN32(g_a g_i) acc),
+ * with the split rule of fp4q_gemm_w4a4, so each segment's columns are those
+ * of fp4q_gemm_w4a4 on that segment alone (bit for bit when both launches
+ * split K alike).  The "Why Gated DeltaNet Survives..." review (section 3)
+ * reports a global-scale mismatch when serving fused GEMMs; a per-segment
+ * scale serves the fused product without requantizing any weight under a
+ * shared scale.
+ *   w_global  device, nseg FP32 (nseg >= 1); with nseg == 0 it is the single
+ *             w_global of fp4q_gemm_w4a4 (device FP32 or NULL = 1.0)
+ *   seg_rows  host, nseg counts >= 0 summing to N (ignored when nseg == 0)
+ * Errors as fp4q_gemm_w4a4; nseg < 0 or > 8 -> ERR_ARG; seg_rows or
+ * w_global NULL with nseg > 0 -> ERR_NULL; a negative count or a sum other
+ * than N -> ERR_SHAPE.
+ */
+fp4q_status fp4q_gemm_w4a4_segmented(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* a_global, fp4q_format fw, const uint8_t* w_codes,
+                                     const uint8_t* w_scales, const float* w_global, const int64_t* seg_rows,
+                                     int nseg, const float* w_special, int64_t M, int64_t N, int64_t K, void* c,
+                                     fp4q_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
+ * W4A4 matmul whose activations arrive in bf16 and are quantized to NVFP4
+ * (block 16) as the matmul loads them: the online activation quantization
+ * ("Finer is Better", Method 2: abs-max or 4-over-6; hierarchical scaling
+ * with a GIVEN global scale) fused into the matmul's A prologue.  The codes,
+ * scales and C are those of fp4q_quantize (NVFP4, block 16, a_rule, GLOBAL
+ * GIVEN a_global, or NONE when a_global is NULL) followed by
+ * fp4q_gemm_w4a4_segmented (C bit for bit when both launches split K alike).
+ * Meant for decode-sized M: every workgroup quantizes the activation rows it
+ * multiplies, so the quantization is repeated once per 128 or 256 output
+ * columns; for large M (prefill) quantize first and call fp4q_gemm_w4a4.
+ *   a            device bf16 (uint16 bit patterns) M x K, pitch lda; 16-byte
+ *                aligned, lda % 8 == 0
+ *   a_rule       FP4Q_RULE_ABSMAX or FP4Q_RULE_4OVER6 (no flags)
+ *   a_global     device FP32 (GIVEN) or NULL (g = 1)
+ *   a_codes_out, a_scales_out  device M x K/2 and M x K/16 bytes, 16-byte
+ *                aligned, written with the quantized activations; or both NULL
+ *   fw           NVFP4, RAZER_A or RAZER_W (block 16); w_global, seg_rows,
+ *                nseg as fp4q_gemm_w4a4_segmented; w_special as fp4q_gemm_w4a4
+ * Errors: NULL pointer (or only one of the two outputs) -> ERR_NULL; another
+ * fw -> ERR_FORMAT; M, N < 0, K <= 0, K % 512, K > 2^24, lda < K, lda > 2^24
+ * or ldc < N -> ERR_SHAPE; another rule, a bad special value or segment
+ * count -> ERR_ARG; misalignment -> ERR_ALIGN.  M == 0 or N == 0 enqueues
+ * nothing.
+ */
+fp4q_status fp4q_gemm_w4a4_act_bf16(const uint16_t* a, int64_t lda, uint32_t a_rule, const float* a_global,
+                                    uint8_t* a_codes_out, uint8_t* a_scales_out, fp4q_format fw,
+                                    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                    const int64_t* seg_rows, int nseg, const float* w_special, int64_t M,
+                                    int64_t N, int64_t K, void* c, fp4q_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
  * Weight-only matmul C = g_w * A W^^T with bf16 activations A (M x K, row
  * pitch lda elements) and a block-16 weight W^ (N x K) in NVFP4 or RAZER_W
  * (RaZeR summary 2.3: the weight-only kernel next to the weight-activation

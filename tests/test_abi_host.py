@@ -79,6 +79,9 @@ L.fp4q_gemm_w4a4.argtypes = [ci, vp, vp, vp, ci, vp, vp, vp, vp, i64, i64, i64, 
 L.fp4q_gemm_w4a4_noalloc.argtypes = L.fp4q_gemm_w4a4.argtypes
 L.fp4q_channel_scale.argtypes = [vp, ci, i64, i64, vp, ci, i64, i64, i64, ctypes.c_double, vp, vp, vp]
 L.fp4q_macaq_quantize.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+L.fp4q_gemm_w4a4_segmented.argtypes = [ci, vp, vp, vp, ci, vp, vp, vp, vp, ci, vp, i64, i64, i64, vp, ci, i64, vp]
+L.fp4q_gemm_w4a4_act_bf16.argtypes = [vp, i64, ctypes.c_uint32, vp, vp, vp, ci, vp, vp, vp, vp, ci, vp, i64, i64, i64,
+                                      vp, ci, i64, vp]
 L.fp4q_gemm_w4a16.argtypes = [vp, i64, ci, vp, vp, vp, vp, i64, i64, i64, vp, ci, i64, vp]
 L.fp4q_razer_table_search.argtypes = [vp, ci, i64, i64, i64, ci, vp, vp, vp, vp, ctypes.c_size_t, vp]
 P = 0x100000  # aligned fake device address; never dereferenced on any error path
@@ -111,6 +114,13 @@ def gn(fa=0, fw=0, a=P, sa=P, w=P, sw=P, sp=None, M=8, N=8, K=64, c=P, ct=0, ldc
 
 def mq(w=P, N=4, K=64, ldw=64, h=P, ldh=64, mm=10, codes=P, scales=P, moves=None, ws=P, wsb=1 << 20):
     return L.fp4q_macaq_quantize(w, N, K, ldw, h, ldh, mm, codes, scales, moves, ws, wsb, None)
+
+SEG = (ctypes.c_int64 * 3)(4, 2, 2)
+def sg(fa=0, fw=0, g=P, seg=ctypes.cast(SEG, vp), nseg=3, M=8, N=8, K=64, c=P, ldc=8):
+    return L.fp4q_gemm_w4a4_segmented(fa, P, P, None, fw, P, P, g, seg, nseg, None, M, N, K, c, 0, ldc, None)
+
+def ab(a=P, lda=512, rule=1, co=None, so=None, fw=0, g=P, seg=None, nseg=0, sp=None, M=8, N=8, K=512, c=P, ldc=8):
+    return L.fp4q_gemm_w4a4_act_bf16(a, lda, rule, None, co, so, fw, P, P, g, seg, nseg, sp, M, N, K, c, 0, ldc, None)
 
 def wa(a=P, lda=512, fw=0, w=P, sw=P, g=None, sp=None, M=8, N=8, K=512, c=P, ct=0, ldc=8):
     return L.fp4q_gemm_w4a16(a, lda, fw, w, sw, g, sp, M, N, K, c, ct, ldc, None)
@@ -171,6 +181,14 @@ res = {
  "w_K": wa(K=256, lda=256), "w_lda": wa(lda=256), "w_lda_big": wa(lda=(1 << 24) + 8), "w_ldc": wa(ldc=4),
  "w_M": wa(M=-1), "w_align_a": wa(a=P + 8), "w_align_lda": wa(lda=516), "w_align_sw": wa(sw=P + 4),
  "w_dtype": wa(ct=2), "w_special": wa(fw=3, sp=ctypes.cast((ctypes.c_float * 4)(5.0, -5.0, 4.0, -2.5), vp)),
+ # segmented matmul
+ "s_nseg": sg(nseg=9), "s_nseg_neg": sg(nseg=-1), "s_null_seg": sg(seg=None), "s_null_g": sg(g=None),
+ "s_sum": sg(N=9, ldc=12), "s_neg": sg(seg=ctypes.cast((ctypes.c_int64 * 3)(4, -2, 6), vp)),
+ "s_align": sg(g=P + 2), "s_mixed": sg(fa=1), "s_K": sg(K=24),
+ # matmul quantizing bf16 activations on load
+ "a_null_a": ab(a=None), "a_one_out": ab(co=P), "a_rule": ab(rule=2), "a_rule_flag": ab(rule=0x101),
+ "a_fw_mx": ab(fw=1), "a_K": ab(K=256, lda=256), "a_lda": ab(lda=256), "a_align": ab(co=P + 4, so=P),
+ "a_lda_align": ab(lda=516), "a_seg": ab(seg=ctypes.cast(SEG, vp), nseg=3, N=7), "a_sp": ab(fw=3),
  # special-value search
  "t_null_w": ts(w=None), "t_null_w0": ts(w=None, rows=0, ws=None, gmode=5), "t_null_table": ts(table=None), "t_null_g": ts(g=None), "t_null_ws": ts(ws=None),
  "t_cols": ts(cols=40, ld=40), "t_ld": ts(ld=32), "t_rows": ts(rows=-1), "t_ws": ts(wsb=4 * 28 * 8 - 8),
@@ -202,6 +220,10 @@ EXPECTED = {
     "m_align": 3,
     "w_null_a": 1, "w_null_sp": 1, "w_format_mx": 4, "w_format_ra": 4, "w_K": 2, "w_lda": 2, "w_lda_big": 2,
     "w_ldc": 2, "w_M": 2, "w_align_a": 3, "w_align_lda": 3, "w_align_sw": 3, "w_dtype": 5, "w_special": 5,
+    "s_nseg": 5, "s_nseg_neg": 5, "s_null_seg": 1, "s_null_g": 1, "s_sum": 2, "s_neg": 2, "s_align": 3,
+    "s_mixed": 4, "s_K": 2,
+    "a_null_a": 1, "a_one_out": 1, "a_rule": 5, "a_rule_flag": 5, "a_fw_mx": 4, "a_K": 2, "a_lda": 2, "a_align": 3,
+    "a_lda_align": 3, "a_seg": 2, "a_sp": 1,
     "t_null_w": 1, "t_null_w0": 5, "t_null_table": 1, "t_null_g": 1, "t_null_ws": 1, "t_cols": 2, "t_ld": 2, "t_rows": 2,
     "t_ws": 5, "t_mode": 5, "t_dtype": 5, "t_align": 3, "t_align_w": 3,
     "c_null": 1, "c_rows": 2, "c_ld": 2, "c_alpha": 5,
@@ -224,8 +246,8 @@ def test_zero_rows_and_empty_gemm_enqueue_nothing():
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     code = f"ROOT = {ROOT!r}\nLIB = {LIB!r}\n" + CHILD.split("res = {")[0] + textwrap.dedent('''
 print(q(rows=0), dq(rows=0), gm(M=0), gm(N=0), q(d=desc(global_mode=1), rows=0), gn(M=0), mq(N=0), wa(M=0),
-      wa(N=0))
+      wa(N=0), sg(M=0), ab(M=0))
 ''')
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == ["0"] * 9
+    assert out.stdout.split() == ["0"] * 11
