@@ -282,10 +282,228 @@ class Marks:
         return out
 
 
+# ---------------------------------------------------------------- the other rows, measured beside the step
+def event_ms(fn, reps: int = 3) -> float:
+    """milliseconds per call of a long-running fn (HIP events on the current stream)"""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def rate(nbytes=None, flops=None, us=None, peak_tf=None):
+    out = {"us": round(us, 2)}
+    if nbytes is not None:
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out.update({"bytes": int(nbytes), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+    if flops is not None:
+        tf = flops / (us * 1e-6) / 1e12
+        out.update({"flops": flops, "TFLOP/s": round(tf, 1)})
+        if peak_tf:
+            out["frac_mfma"] = round(tf / peak_tf, 4)
+    return out
+
+
+def measure_mxfp4_linear(B) -> dict:
+    """4096 x 4096 bf16 activations with 8 outlier channels: channel scale +
+    block-Hadamard 32 + MXFP4 quantize (standard exponent, and the
+    exponent-offset search), then the 4096 x 14336 x 4096 MXFP4 GEMM, fp32 out"""
+    import torch
+    wl = MxLinear(B)
+    qb = wl.quant_bytes
+    t_q = graph_us(wl.quantize_call)
+    t_qs = graph_us(lambda: B.quantize(wl.x, "mxfp4", 32, "expsearch", "none", chan_scale=wl.t, hadamard=32,
+                                       codes=wl.codes, scales=wl.scales))
+    wl.quantize_call()
+    t_g = event_ms(lambda: wl.gemm_calls(), reps=10) * 1e3
+    res = {"workload": wl.config()["workload"], "quantize": {"kernel": "mx32_kernel", **rate(qb, us=t_q)},
+           "quantize_expsearch": rate(qb, us=t_qs),
+           "gemm": {"kernel": "gemm_tile_kernel", **rate(flops=wl.gemm_flops[0], us=t_g,
+                                                         peak_tf=MFMA_PEAK_TFLOPS["fp4"])}}
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_decode(B) -> dict:
+    """The RaZeR decode layer (K 5120, N 17408) at M = 1, 16, 128: RaZeR-A
+    quantize + RaZeR-A x RaZeR-W GEMM; the weight-only matmul on bf16
+    activations; the NVFP4 4-over-6 activation quantize fused into the
+    matmul against the same weight, beside the two launches it replaces; a
+    fused three-way projection (segments 4096/1024/1024 rows of 5120, each
+    under its own global scale) beside the plain matmul of the same shape.
+    Graph-timed.  The weight stream (codes + scales, read once per launch)
+    sets each matmul's HBM floor."""
+    import torch
+    wl = RazerDecode(B, 128)
+    res = {"workload": "razer_decode_K5120_N17408", "weight_bytes": wl.N * wl.K // 2 + wl.N * wl.K // 16,
+           "cases": wl.small_m((1, 16, 128))}
+    w_bytes = res["weight_bytes"]
+    _, _, g_a = B.quantize(wl.x, "nvfp4", 16, "4over6", "auto")
+    for c in res["cases"]:
+        M = c["M"]
+        x = wl.x[:M]
+        out = torch.empty((M, wl.N), dtype=torch.float32, device="cuda")
+        codes = torch.empty((M, wl.K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((M, wl.K // 16), dtype=torch.uint8, device="cuda")
+        t_w16 = graph_us(lambda: B.gemm_w4a16(x, "razer_w", wl.wc, wl.ws, wl.wg, wl.sp, out=out))
+        t_fused = graph_us(lambda: B.gemm_act_bf16(x, "4over6", g_a, "razer_w", wl.wc, wl.ws, wl.wg, None, wl.sp,
+                                                   out=out))
+        t_q = graph_us(lambda: B.quantize(x, "nvfp4", 16, "4over6", "given", global_=g_a, codes=codes,
+                                          scales=scales))
+        B.quantize(x, "nvfp4", 16, "4over6", "given", global_=g_a, codes=codes, scales=scales)
+        t_g = graph_us(lambda: B.gemm("nvfp4", codes, scales, g_a, "razer_w", wl.wc, wl.ws, wl.wg, wl.sp, out=out))
+        c["w4a16"] = {"kernel": "gemm_small_m_kernel (bf16 A)", **rate(w_bytes + M * wl.K * 2, us=t_w16)}
+        c["act_quantized_on_load"] = {"kernel": "gemm_small_m_kernel (A quantized on load)",
+                                      **rate(w_bytes + M * wl.K * 2, us=t_fused),
+                                      "separate_quantize_us": round(t_q, 2), "separate_gemm_us": round(t_g, 2)}
+    # fused projection with per-segment global scales (M = 16), nvfp4 weights
+    M, segs = 16, [4096, 1024, 1024]
+    N = sum(segs)
+    w = torch.randn((N, wl.K), device="cuda") * 0.02
+    wc, ws, wg = B.quantize(w, "nvfp4", 16, "absmax", "auto")
+    del w
+    gs = torch.stack([wg[0], wg[0] * 2, wg[0] * 0.5])
+    ca, sa, ga = B.quantize(wl.x[:M], "nvfp4", 16, "absmax", "auto")
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    t_seg = graph_us(lambda: B.gemm_segmented("nvfp4", ca, sa, ga, "nvfp4", wc, ws, gs, segs, None, out=out))
+    t_one = graph_us(lambda: B.gemm("nvfp4", ca, sa, ga, "nvfp4", wc, ws, wg, None, out=out))
+    res["segmented_projection"] = {"M": M, "segments": segs, "K": wl.K, "segmented_us": round(t_seg, 2),
+                                   "single_scale_us": round(t_one, 2)}
+    # offline special-value search over the same 17408 x 5120 weight (fp32)
+    wf = torch.from_numpy(__import__("datagen").razer_decode(1)["W"]).cuda()
+    t_s = event_ms(lambda: B.razer_table_search(wf, "auto"), reps=3) * 1e3
+    table, _, _ = B.razer_table_search(wf, "auto")
+    res["table_search"] = {"kernel": "razer_search_rows_kernel", "shape": list(wf.shape),
+                           **rate(wf.numel() * 4, us=t_s), "table": [float(v) for v in table.cpu()]}
+    del wf, wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_variants(B) -> dict:
+    """The scale-format variants on 4096 x 4096 FP32 normal samples (block
+    16 unless stated): UE5M3 scales (4-over-6, no global), NVFP4 4-over-6
+    after a size-16 block-Hadamard (given global), MXFP4 exponent-offset
+    search (block 32); graph-timed, algorithmic bytes = input + codes + scales"""
+    import torch
+    import datagen
+    x = torch.from_numpy(datagen.sweep("normal")).cuda()
+    R, C = x.shape
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+    s16 = torch.empty((R, C // 16), dtype=torch.uint8, device="cuda")
+    s32 = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
+    g = torch.full((1,), float(x.abs().max()) / 2688.0, device="cuda")
+    b16, b32 = R * C * 4 + R * C // 2 + R * C // 16, R * C * 4 + R * C // 2 + R * C // 32
+    out = {"workload": "scale_variants_4096x4096_f32"}
+    out["ue5m3_4over6"] = rate(b16, us=graph_us(lambda: B.quantize(x, "ue5m3", 16, "4over6", "none", codes=codes,
+                                                                     scales=s16)))
+    out["nvfp4_had16_4over6"] = rate(b16, us=graph_us(lambda: B.quantize(x, "nvfp4", 16, "4over6", "given",
+                                                                           hadamard=16, global_=g, codes=codes,
+                                                                           scales=s16)))
+    out["nvfp4_4over6"] = rate(b16, us=graph_us(lambda: B.quantize(x, "nvfp4", 16, "4over6", "given", global_=g,
+                                                                     codes=codes, scales=s16)))
+    out["mxfp4_expsearch"] = rate(b32, us=graph_us(lambda: B.quantize(x, "mxfp4", 32, "expsearch", "none",
+                                                                        codes=codes, scales=s32)))
+    out["mxfp4_absmax"] = rate(b32, us=graph_us(lambda: B.quantize(x, "mxfp4", 32, "absmax", "none", codes=codes,
+                                                                     scales=s32)))
+    del x
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_macaq(B) -> dict:
+    """MACaQ calibration of a 1024 x 4096 slice of the MXFP4 linear weight
+    (N(0, 0.02)) with the binary64 Hessian X^T X of 4096 synthetic
+    activation rows (the MXFP4 linear recipe: normal with 8 outlier
+    channels), move cap 2K per row; one call timed with HIP events"""
+    import torch
+    import datagen
+    d = datagen.mxfp4_linear(4096, 4096, 1024)
+    X = torch.from_numpy(datagen.bf16_bits_to_f32(d["X_bf16"])).cuda().double()
+    H = X.T @ X
+    W = torch.from_numpy(d["W"]).cuda()
+    del X
+    t = event_ms(lambda: B.macaq_quantize(W, H), reps=1)
+    _, _, moves = B.macaq_quantize(W, H)
+    torch.cuda.synchronize()
+    res = {"workload": "macaq_N1024_K4096", "ms": round(t, 2), "rows_per_s": round(1024 / (t * 1e-3), 1),
+           "mean_moves_per_row": round(float(moves.double().mean()), 1)}
+    del W, H
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------- CPU baseline
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def cpu_baseline_parallel(wl, threads: int, budget_s: float = 10.0):
+    """The same oracle calls on `threads` threads at once, each on its own
+    rows (the oracle's C functions run without the interpreter lock): the
+    quantize of 32 rows per thread and one activation row against 512
+    replicated weight rows per thread, repeated for the budget; per-element
+    and per-MAC times from the aggregate, extrapolated to one whole step."""
+    import concurrent.futures as cf
+    import datagen
+    import oracle as O
+    K = wl.K
+    a = datagen.prefill_act(32 * threads, K)
+    g = float(wl.g_act.item())
+    codes, scales = O.quantize_rows(O.transform(a[:2]), "nvfp4", 16, O.FOUR_OVER_SIX, g)
+    wsamp = [O.quantize_rows(datagen.normal((1, K), 12 + i, 0.02), "nvfp4", 16, O.FOUR_OVER_SIX, 1e-4)
+             for i in range(len(wl.NS))]
+    xt = O.transform(a)
+
+    def q_job(i):
+        O.quantize_rows(xt[32 * i:32 * i + 32], "nvfp4", 16, O.FOUR_OVER_SIX, g)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(q_job, range(threads)))
+        tq = (time.perf_counter() - t0) / (32 * threads * K)
+
+        per_mac = []
+        for (wc1, ws1) in wsamp:
+            wc = np.repeat(wc1, 512, axis=0)
+            ws = np.repeat(ws1, 512, axis=0)
+
+            def g_job(_):
+                n, t1 = 0, time.perf_counter()
+                while time.perf_counter() - t1 < budget_s / (2 * len(wl.NS)):
+                    O.gemm_rows("nvfp4", codes, scales, 1.0, "nvfp4", wc, ws, 1.0, None, 2, 512, K, 0, 1)
+                    n += 512 * K
+                return n
+
+            t0 = time.perf_counter()
+            done = sum(ex.map(g_job, range(threads)))
+            per_mac.append((time.perf_counter() - t0) / done)
+    return tq * wl.M * K + sum(tm * wl.M * n * K for tm, n in zip(per_mac, wl.NS))
+
+
 def cpu_baseline(wl, budget_s: float = 20.0):
     """The oracle, as it is, on a bounded sample of the same workload, single
-    thread; extrapolated linearly to one whole step."""
+    thread; extrapolated linearly to one whole step.  For the prefill step
+    also on the host's cores at once (at most 16 threads)."""
     import datagen
     import oracle as O
     O.build()
@@ -337,7 +555,8 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         t_gemm_per_mac.append((time.perf_counter() - t0) / done)
     t_step = tq * wl.M * K + sum(tm * wl.M * n * K for tm, n in zip(t_gemm_per_mac, wl.NS))
     flops = sum(wl.gemm_flops)
-    return {
+    model, ncpu = cpu_info()
+    out = {
         "value": flops / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": 1,
@@ -346,7 +565,18 @@ def cpu_baseline(wl, budget_s: float = 20.0):
                    f"2048 weight rows per projection repeated for ~{budget_s / 2:.0f} s; per-element and per-MAC "
                    f"times extrapolated linearly to the full step"),
         "step_s_extrapolated": t_step,
+        "cpu_model": model,
+        "host_cpus": ncpu,
     }
+    if isinstance(wl, Prefill) and ncpu > 1:
+        threads = min(ncpu, 16)
+        t_par = cpu_baseline_parallel(wl, threads)
+        out.update({"value": flops / t_par / 1e12, "cores": threads, "step_s_extrapolated": t_par,
+                    "single_thread_value": flops / t_step / 1e12,
+                    "sample": out["sample"] + f"; value: the same oracle on {threads} threads at once, "
+                              f"each on its own rows (32 quantized rows and 1 x 512 GEMM rows per thread, "
+                              f"~{10:.0f} s)"})
+    return out
 
 
 # ---------------------------------------------------------------- traffic from PMC runs
@@ -468,6 +698,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other rows (MXFP4 linear, decode batch sizes, variants, MACaQ, search)")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-scaling copy kernel and exit")
     ap.add_argument("--quant-sweep", action="store_true",
                     help="time the NVFP4 quantizer over rules x block sizes on 4096 x 4096 FP32, print one JSON line, exit")
@@ -583,6 +815,16 @@ def main():
     if isinstance(wl, RazerDecode):
         log("[bench] decode batch sizes")
         out["decode_small_m"] = wl.small_m()
+    if not args.no_rows and isinstance(wl, Prefill):
+        # the other rows of the path, each at its own workload, on the same GPU after the step
+        del wl.w
+        torch.cuda.empty_cache()
+        rows = {}
+        for name, fn in (("mxfp4_linear", measure_mxfp4_linear), ("razer_decode", measure_decode),
+                         ("scale_variants", measure_variants), ("macaq", measure_macaq)):
+            log(f"[bench] row {name}")
+            rows[name] = fn(B)
+        out["rows"] = rows
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl)
