@@ -743,11 +743,14 @@ int mx32_grid(int64_t rows, int64_t rpr) {
 // block (RaZeR-W: abs-max E3M3 scale under g) takes the table's value with the
 // lowest block error, and a table's tensor error is the binary64 sum over
 // rows (ascending) of the binary64 sum over each row's blocks (ascending).
-// One thread per row: it forms the block's error for each of the 16 signed
-// candidates (the block error of RaZeR-W quantization), then, per pair, adds
-// the smallest of its four to the row's 28 sums.
+// One wave per row, one lane per block of a 64-block chunk: the lane forms
+// the block error of each of the 16 signed candidates (the block error of
+// RaZeR-W quantization) and the 28 pair minima; the wave stages the minima in
+// LDS and lanes 0..27 add their pair's column in block order.
 constexpr int kSearchCand = 8, kSearchPairs = kRazerPairs;
-constexpr float kSearchMag[kSearchCand] = {2.5f, 3.5f, 4.5f, 5.0f, 5.5f, 6.5f, 7.0f, 7.5f};
+// the candidate magnitudes times 2, one nibble each: 5, 7, 9, 10, 11, 13, 14, 15
+constexpr uint32_t kSearchMag2 = 0xFEDBA975u;
+__host__ __device__ constexpr float search_mag(int i) { return 0.5f * (float)((kSearchMag2 >> (4 * i)) & 15u); }
 
 struct SearchTables {
   uint32_t elt[64][8];                // per E3M3 code: 7 element thresholds (strict >)
@@ -756,9 +759,12 @@ struct SearchTables {
   uint32_t hi[64][kSearchCand];       // ... strict <
 };
 
+constexpr int kSearchWaves = kThreads / 64;  // rows per workgroup
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void razer_search_rows_kernel(QuantParams p, double* row_sums) {
   __shared__ SearchTables T;
+  __shared__ float mins[kSearchWaves][kSearchPairs][64];
   const float g = p.global ? *p.global : 1.0f;
   const double gd = (double)g;
   for (int k = threadIdx.x; k < 64; k += blockDim.x) {
@@ -770,21 +776,26 @@ __global__ __launch_bounds__(kThreads) void razer_search_rows_kernel(QuantParams
     for (int c = 0; c < kSearchCand; ++c) {
       float lo, hi;
       bool open_hi;
-      special_bounds(kSearchMag[c], lo, hi, open_hi);
+      special_bounds(search_mag(c), lo, hi, open_hi);
       T.lo[k][c] = k == 0 ? 0x7F800000u : thr_bits((double)lo * sg, false);
       T.hi[k][c] = (k == 0 || open_hi) ? 0x7F800000u : ru_bits((double)hi * sg);
     }
   }
   __syncthreads();
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= p.rows) return;  // no barrier follows
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * kSearchWaves + wave;
+  const bool live = r0 < p.rows;
+  const int64_t r = live ? r0 : p.rows - 1;  // waves past the end read the last row and write nothing
   const double inv6 = 1.0 / (6.0 * gd);
-  double sums[kSearchPairs];
-#pragma unroll
-  for (int q = 0; q < kSearchPairs; ++q) sums[q] = 0.0;
-  for (int64_t b = 0; b < p.cols / 16; ++b) {
+  const int64_t nb = p.cols / 16;
+  double acc = 0.0;  // lanes 0..27: pair `lane`
+  // every wave of the workgroup runs the same chunks (equal rows), so the
+  // workgroup barriers below are reached by all
+  for (int64_t b0 = 0; b0 < nb; b0 += 64) {
+    const int64_t b = b0 + lane;
+    const bool has = b < nb;
     Raw<16, BF16> raw;
-    load_raw<16, BF16>(p, r, 16 * b, raw);
+    load_raw<16, BF16>(p, r, 16 * (has ? b : nb - 1), raw);
     float x[16];
     finish_chunk<16, BF16, false>(p, 16 * b, raw, x, false, 0);
     uint32_t amax = 0;
@@ -792,47 +803,109 @@ __global__ __launch_bounds__(kThreads) void razer_search_rows_kernel(QuantParams
     for (int i = 0; i < 16; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
     const int k = select_scale<1>(bitsf(amax), T.smid6, inv6);
     const float s = (float)sf_val<1>(k);
-    uint32_t t[7];
+    // thresholds in scalars: an array read through selected elements would
+    // be placed in memory
+    const uint32_t t0 = T.elt[k][0], t1 = T.elt[k][1], t2 = T.elt[k][2], t3 = T.elt[k][3], t4 = T.elt[k][4],
+                   t5 = T.elt[k][5], t6 = T.elt[k][6];
+    // the standard codes, then per candidate the RaZeR element rule of
+    // encode_special: 0x8 inside the special value's interval with its sign
+    uint32_t std0 = 0, std1 = 0;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) t[j] = T.elt[k][j];
-    float err[2 * kSearchCand];
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t bb = fbits(x[i]);
+      const int mm = rtn_mag_v(bb & 0x7FFFFFFFu, t0, t1, t2, t3, t4, t5, t6);
+      const uint32_t cc = mm ? ((uint32_t)mm | ((bb >> 28) & 8u)) : 0u;
+      if (i < 8) std0 |= cc << (4 * i);
+      else std1 |= cc << (4 * (i - 8));
+    }
+    float m[kSearchCand];  // per magnitude: the smaller block error of its two signs
 #pragma unroll
     for (int c = 0; c < kSearchCand; ++c) {
+      const uint32_t lo = T.lo[k][c], hi = T.hi[k][c];
+      float e2[2];
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg) {
-        const float v = sg ? -kSearchMag[c] : kSearchMag[c];
         const uint32_t vsign = sg ? 0x80000000u : 0u;
-        const uint32_t p0 = k ? encode_special<8>(x, t, T.lo[k][c], T.hi[k][c], vsign) : 0u;
-        const uint32_t p1 = k ? encode_special<8>(x + 8, t, T.lo[k][c], T.hi[k][c], vsign) : 0u;
-        err[2 * c + sg] = lane_sse<8>(x, p0, s, g, true, v * s) + lane_sse<8>(x + 8, p1, s, g, true, v * s);
+        uint32_t p0 = std0, p1 = std1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t bb = fbits(x[i]), xb = bb & 0x7FFFFFFFu;
+          const bool sp = ((bb & 0x80000000u) == vsign) && xb > lo && xb < hi;
+          if (i < 8) p0 = sp ? ((p0 & ~(0xFu << (4 * i))) | (8u << (4 * i))) : p0;
+          else p1 = sp ? ((p1 & ~(0xFu << (4 * (i - 8)))) | (8u << (4 * (i - 8)))) : p1;
+        }
+        if (k == 0) p0 = p1 = 0u;
+        const float v = sg ? -search_mag(c) : search_mag(c);
+        e2[sg] = lane_sse<8>(x, p0, s, g, true, v * s) + lane_sse<8>(x + 8, p1, s, g, true, v * s);
       }
+      m[c] = fminf(e2[0], e2[1]);
     }
-    int q = 0;
+    {
+      int q = 0;
 #pragma unroll
-    for (int i = 0; i < kSearchCand; ++i)
+      for (int i = 0; i < kSearchCand; ++i)
 #pragma unroll
-      for (int j = i + 1; j < kSearchCand; ++j, ++q) {
-        const float m = fminf(fminf(err[2 * i], err[2 * i + 1]), fminf(err[2 * j], err[2 * j + 1]));
-        sums[q] = sums[q] + (double)m;
-      }
+        for (int j = i + 1; j < kSearchCand; ++j, ++q) mins[wave][q][lane] = fminf(m[i], m[j]);
+    }
+    __syncthreads();
+    if (lane < kSearchPairs) {
+      const int n = (int)min((int64_t)64, nb - b0);
+      for (int l = 0; l < n; ++l) acc = acc + (double)mins[wave][lane][l];
+    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int q = 0; q < kSearchPairs; ++q) row_sums[r * kSearchPairs + q] = sums[q];
+  if (live && lane < kSearchPairs) row_sums[r * kSearchPairs + lane] = acc;
 }
 
 // per pair, the sum over rows in ascending order; then the smallest (a tie
-// keeps the earlier pair) as the table {+a, -a, +b, -b}
-__global__ void razer_search_reduce_kernel(const double* row_sums, int64_t rows, double* pair_sse, float* table) {
+// keeps the earlier pair) as the table {+a, -a, +b, -b}.  The workgroup
+// stages 128 rows of sums at a time in LDS with coalesced loads (the next
+// chunk's loads in flight while the current one is summed); threads 0..27
+// add their pair's column in row order.
+constexpr int kReduceRows = 128;
+__global__ __launch_bounds__(256) void razer_search_reduce_kernel(const double* row_sums, int64_t rows,
+                                                                  double* pair_sse, float* table) {
+  __shared__ double buf[2][kReduceRows * kSearchPairs];
   __shared__ double tot[kSearchPairs];
-  const int q = threadIdx.x;
-  if (q < kSearchPairs) {
-    double acc = 0.0;
-    for (int64_t r = 0; r < rows; ++r) acc = acc + row_sums[r * kSearchPairs + q];
-    tot[q] = acc;
-    pair_sse[q] = acc;
+  const int tid = threadIdx.x;
+  constexpr int kChunk = kReduceRows * kSearchPairs;  // doubles per chunk
+  const int64_t total = rows * kSearchPairs;
+  const int64_t nchunks = (rows + kReduceRows - 1) / kReduceRows;
+  double acc = 0.0;
+  double pre[(kChunk + 255) / 256];
+  auto fetch = [&](int64_t ch) {
+#pragma unroll
+    for (int i = 0; i < (kChunk + 255) / 256; ++i) {
+      const int64_t idx = ch * kChunk + i * 256 + tid;
+      pre[i] = (i * 256 + tid < kChunk && idx < total) ? row_sums[idx] : 0.0;
+    }
+  };
+  auto stage = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < (kChunk + 255) / 256; ++i)
+      if (i * 256 + tid < kChunk) buf[slot][i * 256 + tid] = pre[i];
+  };
+  if (nchunks > 0) fetch(0);
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int slot = (int)(ch & 1);
+    stage(slot);
+    __syncthreads();
+    if (ch + 1 < nchunks) fetch(ch + 1);  // in flight while the column sums run
+    if (tid < kSearchPairs) {
+      const int64_t n = min((int64_t)kReduceRows, rows - ch * kReduceRows);
+#pragma unroll 8
+      for (int64_t r = 0; r < n; ++r) acc = acc + buf[slot][r * kSearchPairs + tid];
+    }
+    // the slot written next iteration is the other one; the one after that
+    // waits for this barrier
+    __syncthreads();
+  }
+  if (tid < kSearchPairs) {
+    tot[tid] = acc;
+    pair_sse[tid] = acc;
   }
   __syncthreads();
-  if (q == 0) {
+  if (tid == 0) {
     int best = 0;
     for (int i = 1; i < kSearchPairs; ++i)
       if (tot[i] < tot[best]) best = i;
@@ -840,10 +913,10 @@ __global__ void razer_search_reduce_kernel(const double* row_sums, int64_t rows,
     for (int i = 0; i < kSearchCand; ++i)
       for (int j = i + 1; j < kSearchCand; ++j, ++n)
         if (n == best) {
-          table[0] = kSearchMag[i];
-          table[1] = -kSearchMag[i];
-          table[2] = kSearchMag[j];
-          table[3] = -kSearchMag[j];
+          table[0] = search_mag(i);
+          table[1] = -search_mag(i);
+          table[2] = search_mag(j);
+          table[3] = -search_mag(j);
         }
   }
 }
@@ -1169,12 +1242,12 @@ hipError_t launch_razer_search(const QuantParams& p, int gmode, double* row_sums
     const hipError_t e = launch_auto_global(p, 180.0f, s);
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = (unsigned)((p.rows + kThreads - 1) / kThreads);
+  const unsigned grid = (unsigned)((p.rows + kSearchWaves - 1) / kSearchWaves);  // one wave per row
   if (p.rows > 0) {
     if (p.x_bf16) hipLaunchKernelGGL(razer_search_rows_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, row_sums);
     else hipLaunchKernelGGL(razer_search_rows_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, row_sums);
   }
-  hipLaunchKernelGGL(razer_search_reduce_kernel, dim3(1), dim3(64), 0, s, (const double*)row_sums, p.rows, pair_sse,
+  hipLaunchKernelGGL(razer_search_reduce_kernel, dim3(1), dim3(256), 0, s, (const double*)row_sums, p.rows, pair_sse,
                      table);
   return hipGetLastError();
 }
