@@ -74,6 +74,16 @@ fp4q_status device_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4
 
 size_t elem_size(fp4q_dtype t) { return t == FP4Q_BF16 ? 2 : 4; }
 
+// A rows x pitch matrix the kernels can address: each extent at most 2^40
+// and the element count at most 2^46 (far above one GPU's memory), so that
+// no byte offset or size formed from them overflows 64 bits.  Checked
+// before any product of the two is formed.
+bool dims_ok(int64_t rows, int64_t pitch) {
+  constexpr int64_t kMaxExtent = int64_t(1) << 40, kMaxElems = int64_t(1) << 46;
+  if (rows < 0 || pitch < 0 || rows > kMaxExtent || pitch > kMaxExtent) return false;
+  return rows == 0 || pitch <= kMaxElems / rows;
+}
+
 // Validation shared by the two matmul entry points, then the launch
 // parameters.  Touches no HIP API.
 fp4q_status gemm_params(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
@@ -87,6 +97,7 @@ fp4q_status gemm_params(fp4q_format fa, const uint8_t* a_codes, const uint8_t* a
   if (fw == FP4Q_NVFP4_RAZER_W && !w_special) return FP4Q_ERR_NULL;
   const int64_t block = fa == FP4Q_MXFP4 ? 32 : 16;
   if (M < 0 || N < 0 || K <= 0 || K % block != 0 || K > (int64_t(1) << 24) || ldc < N) return FP4Q_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, ldc)) return FP4Q_ERR_SHAPE;
   const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   if (tiles_n > 0 && tiles_m > INT32_MAX / tiles_n) return FP4Q_ERR_SHAPE;
   if (fw == FP4Q_NVFP4_RAZER_W)
@@ -147,6 +158,7 @@ fp4q_status fp4q_quantize(const fp4q_quant_desc* desc, const void* x, fp4q_dtype
   if (!x || !codes || !scales) return FP4Q_ERR_NULL;
   if (desc->global_mode != FP4Q_GLOBAL_NONE && !global) return FP4Q_ERR_NULL;
   if (rows < 0 || cols <= 0 || ld_x < cols || cols % desc->block != 0) return FP4Q_ERR_SHAPE;
+  if (!dims_ok(rows, ld_x)) return FP4Q_ERR_SHAPE;
   if (desc->hadamard != 0 && cols % desc->hadamard != 0) return FP4Q_ERR_SHAPE;
   if (!aligned16(x) || (ld_x * (int64_t)elem_size(x_dtype)) % 16 != 0 || !aligned16(codes))
     return FP4Q_ERR_ALIGN;
@@ -179,6 +191,7 @@ fp4q_status fp4q_dequantize(const fp4q_quant_desc* desc, const uint8_t* codes,
   if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
   if (!codes || !scales || !out) return FP4Q_ERR_NULL;
   if (rows < 0 || cols <= 0 || ld_out < cols || cols % desc->block != 0) return FP4Q_ERR_SHAPE;
+  if (!dims_ok(rows, ld_out)) return FP4Q_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(out) || (ld_out * (int64_t)elem_size(out_dtype)) % 16 != 0)
     return FP4Q_ERR_ALIGN;
   if (global && ((uintptr_t)global & 3u)) return FP4Q_ERR_ALIGN;
@@ -251,6 +264,7 @@ fp4q_status fp4q_gemm_w4a4_act_bf16(const uint16_t* a, int64_t lda, uint32_t a_r
   if (M < 0 || N < 0 || K <= 0 || K % 512 != 0 || K > (int64_t(1) << 24) || lda < K || lda > (int64_t(1) << 24) ||
       ldc < N)
     return FP4Q_ERR_SHAPE;
+  if (!dims_ok(M, lda) || !dims_ok(N, K) || !dims_ok(M, ldc)) return FP4Q_ERR_SHAPE;
   if (fw == FP4Q_NVFP4_RAZER_W)
     for (int i = 0; i < 4; ++i)
       if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
@@ -291,6 +305,7 @@ fp4q_status fp4q_gemm_w4a16(const uint16_t* a, int64_t lda, fp4q_format fw, cons
   if (M < 0 || N < 0 || K <= 0 || K % 512 != 0 || K > (int64_t(1) << 24) || lda < K || lda > (int64_t(1) << 24) ||
       ldc < N)
     return FP4Q_ERR_SHAPE;
+  if (!dims_ok(M, lda) || !dims_ok(N, K) || !dims_ok(M, ldc)) return FP4Q_ERR_SHAPE;
   if (fw == FP4Q_NVFP4_RAZER_W)
     for (int i = 0; i < 4; ++i)
       if (!valid_special(w_special[i])) return FP4Q_ERR_ARG;
@@ -322,7 +337,7 @@ fp4q_status fp4q_razer_table_search(const void* w, fp4q_dtype w_dtype, int64_t r
   if (global_mode < FP4Q_GLOBAL_NONE || global_mode > FP4Q_GLOBAL_GIVEN) return FP4Q_ERR_ARG;
   if (!pair_sse || !table) return FP4Q_ERR_NULL;
   if (global_mode != FP4Q_GLOBAL_NONE && !global) return FP4Q_ERR_NULL;
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld_w < cols) return FP4Q_ERR_SHAPE;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld_w < cols || !dims_ok(rows, ld_w)) return FP4Q_ERR_SHAPE;
   if (rows > 0 && (!w || !workspace)) return FP4Q_ERR_NULL;
   if ((uint64_t)rows > (uint64_t)(SIZE_MAX / (kRazerPairs * sizeof(double))) ||
       workspace_bytes < (size_t)rows * kRazerPairs * sizeof(double))
@@ -346,6 +361,7 @@ fp4q_status fp4q_macaq_quantize(const float* w, int64_t N, int64_t K, int64_t ld
                                 int32_t* moves, void* workspace, size_t workspace_bytes, void* stream) {
   if (!w || !h || !codes || !scales || !workspace) return FP4Q_ERR_NULL;
   if (N < 0 || K <= 0 || K % 32 != 0 || K > macaq_max_k() || ldw < K || ldh < K) return FP4Q_ERR_SHAPE;
+  if (!dims_ok(N, ldw) || !dims_ok(K, ldh)) return FP4Q_ERR_SHAPE;
   if (max_moves < 0 || workspace_bytes < (size_t)K * sizeof(double)) return FP4Q_ERR_ARG;
   if (((uintptr_t)w & 3u) || ((uintptr_t)h & 7u) || ((uintptr_t)workspace & 7u) || ((uintptr_t)moves & 3u))
     return FP4Q_ERR_ALIGN;
@@ -371,6 +387,7 @@ fp4q_status fp4q_channel_scale(const void* x, fp4q_dtype x_dtype, int64_t rows_x
     return FP4Q_ERR_ARG;
   if (!x || !w || !t || !r) return FP4Q_ERR_NULL;
   if (rows_x <= 0 || rows_w <= 0 || cols <= 0 || ldx < cols || ldw < cols) return FP4Q_ERR_SHAPE;
+  if (!dims_ok(rows_x, ldx) || !dims_ok(rows_w, ldw)) return FP4Q_ERR_SHAPE;
   if (!std::isfinite(alpha)) return FP4Q_ERR_ARG;
   if (((uintptr_t)x % elem_size(x_dtype)) || ((uintptr_t)w % elem_size(w_dtype)) ||
       ((uintptr_t)t & 3u) || ((uintptr_t)r & 3u))

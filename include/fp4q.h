@@ -46,6 +46,10 @@
  * and returns without synchronising.  An argument error returns its status
  * and enqueues nothing; a failed launch returns FP4Q_ERR_DEVICE.
  *
+ * Sizes: every row count, column count and pitch is at most 2^40 and every
+ * matrix holds at most 2^46 elements (rows x pitch), else FP4Q_ERR_SHAPE, so
+ * that no offset formed from them overflows.
+ *
  * Non-finite inputs, and a GIVEN global scale that is not a positive finite
  * number, are outside the contract: the outputs are then unspecified.
  */
