@@ -579,16 +579,160 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     return out
 
 
+# ---------------------------------------------------------------- per-workload table
+def oracle_times(jobs, threads: int):
+    """seconds per job (zero-argument oracle calls of equal size, on disjoint
+    rows or repeated), run one after another, then the wall time of all of
+    them at once on `threads` threads (the oracle's C functions run without
+    the interpreter lock) divided by their number: the time per job's worth
+    of work on that many cores"""
+    import concurrent.futures as cf
+    t0 = time.perf_counter()
+    for j in jobs:
+        j()
+    single = (time.perf_counter() - t0) / len(jobs)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda j: j(), jobs))
+        par = time.perf_counter() - t0
+    return single, par / len(jobs)
+
+
+def config_table(B) -> dict:
+    """GPU time and oracle time for each workload's quantize and GEMM: the GPU
+    graph- or event-timed at full size; the oracle on row samples (stated
+    per entry), single thread and on up to 16 host threads at once,
+    extrapolated linearly to the full size"""
+    import torch
+    import datagen
+    import oracle as O
+    O.build()
+    model, ncpu = cpu_info()
+    threads = max(1, min(16, ncpu))
+    out = {"cpu_model": model, "host_cpus": ncpu, "threads": threads, "rows": []}
+
+    def add(cfg, op, gpu_us, work, unit, sample, jobs, scale):
+        """jobs: `threads` oracle calls of equal size; scale: full work / one call's work"""
+        one, par = oracle_times(jobs, threads)
+        rate = lambda sec: work / sec / (1e9 if unit == "GB/s" else 1e12)
+        out["rows"].append({"config": cfg, "op": op, "gpu_us": round(gpu_us, 2),
+                            f"gpu_{unit}": round(rate(gpu_us * 1e-6), 2),
+                            "oracle_1t_s": round(one * scale, 3), f"oracle_1t_{unit}": rate(one * scale),
+                            f"oracle_{threads}t_s": round(par * scale, 3),
+                            f"oracle_{threads}t_{unit}": rate(par * scale), "oracle_sample": sample})
+        log(f"[table] {cfg} {op}: gpu {gpu_us:.1f} us, oracle {one * scale:.2f} s (1 thread)")
+
+    # C1: tiny
+    d = datagen.tiny()
+    W, A = torch.from_numpy(d["W"]).cuda(), torch.from_numpy(d["A"]).cuda()
+    for rule, orule in (("absmax", O.ABSMAX), ("4over6", O.FOUR_OVER_SIX), ("brute", O.BRUTE)):
+        t = graph_us(lambda: B.quantize(W, "nvfp4", 16, rule, "none"))
+        nb = 256 * 256 * 4 + 256 * 128 + 256 * 16
+        add("tiny", f"quantize W 256x256 nvfp4 {rule}", t, nb, "GB/s", "whole tensor",
+            [lambda: O.quantize(d["W"], "nvfp4", 16, orule, O.G_NONE)] * threads, 1.0)
+    ca, sa, _ = B.quantize(A, "nvfp4", 16, "absmax", "none")
+    cw, sw, _ = B.quantize(W, "nvfp4", 16, "absmax", "none")
+    o = torch.empty((64, 256), device="cuda")
+    t = graph_us(lambda: B.gemm("nvfp4", ca, sa, None, "nvfp4", cw, sw, None, out=o))
+    oca, osa, _ = O.quantize(d["A"], "nvfp4", 16, O.ABSMAX, O.G_NONE)
+    ocw, osw, _ = O.quantize(d["W"], "nvfp4", 16, O.ABSMAX, O.G_NONE)
+    add("tiny", "gemm 64x256x256", t, 2.0 * 64 * 256 * 256, "TFLOP/s", "whole product",
+        [lambda: O.gemm_rows("nvfp4", oca, osa, 1.0, "nvfp4", ocw, osw, 1.0, None, 64, 256, 256)] * threads, 1.0)
+    # C2: sweep (B = 16; the other blocks and rules: --quant-sweep)
+    x_np = datagen.sweep("normal")
+    x = torch.from_numpy(x_np).cuda()
+    g = torch.full((1,), float(np.abs(x_np).max()) / 2688.0, device="cuda")
+    for rule, orule in (("absmax", O.ABSMAX), ("4over6", O.FOUR_OVER_SIX)):
+        t = graph_us(lambda: B.quantize(x, "nvfp4", 16, rule, "given", global_=g))
+        nb = 4096 * 4096 * 4 + 4096 * 2048 + 4096 * 256
+        add("sweep", f"quantize 4096x4096 f32 nvfp4 B16 {rule} given g", t, nb, "GB/s", "64 rows per call",
+            [(lambda i=i: O.quantize_rows(x_np[64 * i:64 * i + 64], "nvfp4", 16, orule, float(g.item())))
+             for i in range(threads)], 4096 / 64)
+    del x
+    # C3: MXFP4 linear
+    wl = MxLinear(B)
+    t = graph_us(wl.quantize_call)
+    dm = datagen.mxfp4_linear(4096, 4096, 16)
+    tt = wl.t.cpu().numpy()
+    add("mxfp4_linear", "act quantize 4096x4096 bf16 mxfp4 D+B", t, wl.quant_bytes, "GB/s", "64 rows per call",
+        [(lambda i=i: O.quantize(dm["X_bf16"][64 * i:64 * i + 64], "mxfp4", 32, O.ABSMAX, O.G_NONE, chan_scale=tt,
+                                 hadamard=32)) for i in range(threads)], 4096 / 64)
+    wl.quantize_call()
+    t = event_ms(lambda: wl.gemm_calls(), reps=10) * 1e3
+    oc, os_, _ = O.quantize(dm["X_bf16"][:2], "mxfp4", 32, O.ABSMAX, O.G_NONE, chan_scale=tt, hadamard=32)
+    w1 = O.quantize_rows(datagen.normal((1, 4096), 6, 0.02), "mxfp4", 32, O.ABSMAX, 1.0)
+    wc, ws = np.repeat(w1[0], 1024, axis=0), np.repeat(w1[1], 1024, axis=0)
+    add("mxfp4_linear", "gemm 4096x14336x4096 f32 out", t, wl.gemm_flops[0], "TFLOP/s",
+        "1 activation row x 1024 weight rows per call",
+        [lambda: O.gemm_rows("mxfp4", oc, os_, 1.0, "mxfp4", wc, ws, 1.0, None, 2, 1024, 4096, 0, 1)] * threads,
+        4096 * 14336 / 1024)
+    del wl
+    torch.cuda.empty_cache()
+    # C4: RaZeR decode
+    dec = RazerDecode(B, 128)
+    for M in (1, 16, 128):
+        xm = dec.x[:M]
+        codes = torch.empty((M, 2560), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((M, 320), dtype=torch.uint8, device="cuda")
+        gq = torch.ones(1, device="cuda")
+        out_m = torch.empty((M, 17408), device="cuda")
+        tq = graph_us(lambda: B.quantize(xm, "razer_a", 16, "absmax", "auto", global_=gq, codes=codes,
+                                         scales=scales))
+        B.quantize(xm, "razer_a", 16, "absmax", "auto", global_=gq, codes=codes, scales=scales)
+        tg = graph_us(lambda: B.gemm("razer_a", codes, scales, gq, "razer_w", dec.wc, dec.ws, dec.wg, dec.sp,
+                                     out=out_m))
+        am = datagen.razer_decode(M, with_weight=False)["A_bf16"]
+        add("razer_decode", f"razer_a quantize {M}x5120 auto g", tq, M * 5120 * 2 + M * 2560 + M * 320, "GB/s",
+            "whole tensor", [lambda: O.quantize(am, "razer_a", 16, O.ABSMAX, O.G_AUTO)] * threads, 1.0)
+        oc, os_, og = O.quantize(am[:1], "razer_a", 16, O.ABSMAX, O.G_AUTO)
+        w1 = O.quantize_rows(datagen.normal((1, 5120), 7, 0.02), "razer_w", 16, O.ABSMAX, 1e-4, dec.sp)
+        wc, ws = np.repeat(w1[0], 1024, axis=0), np.repeat(w1[1], 1024, axis=0)
+        add("razer_decode", f"gemm {M}x17408x5120", tg, 2.0 * M * 17408 * 5120, "TFLOP/s",
+            "1 activation row x 1024 weight rows per call",
+            [lambda: O.gemm_rows("razer_a", oc, os_, og, "razer_w", wc, ws, 1.0, dec.sp, 1, 1024, 5120, 0, 1)]
+            * threads, M * 17408 / 1024)
+    del dec
+    torch.cuda.empty_cache()
+    # C5: prefill
+    pf = Prefill(B)
+    tq = graph_us(pf.quantize_call)
+    ap = datagen.prefill_act(64 * threads, 5120)
+    gp = float(pf.g_act.item())
+    add("prefill", "act quantize 32768x5120 bf16 nvfp4 4over6 given g", tq, pf.quant_bytes, "GB/s",
+        "64 rows per call", [(lambda i=i: O.quantize(ap[64 * i:64 * i + 64], "nvfp4", 16, O.FOUR_OVER_SIX, O.G_GIVEN,
+                                                     g=gp)) for i in range(threads)], 32768 / 64)
+    pf.quantize_call()
+    oc, os_, _ = O.quantize(ap[:1], "nvfp4", 16, O.FOUR_OVER_SIX, O.G_GIVEN, g=gp)
+    for i, (n, (wc_, ws_, wg_, o_)) in enumerate(zip(pf.NS, pf.w)):
+        t = event_ms(lambda: pf.B.gemm("nvfp4", pf.codes, pf.scales, pf.g_act, "nvfp4", wc_, ws_, wg_, out=o_),
+                     reps=5) * 1e3
+        w1 = O.quantize_rows(datagen.normal((1, 5120), 12 + i, 0.02), "nvfp4", 16, O.FOUR_OVER_SIX, 1e-4)
+        wc, ws = np.repeat(w1[0], 1024, axis=0), np.repeat(w1[1], 1024, axis=0)
+        add("prefill", f"gemm 32768x{n}x5120 bf16 out", t, pf.gemm_flops[i], "TFLOP/s",
+            "1 activation row x 1024 weight rows per call",
+            [lambda: O.gemm_rows("nvfp4", oc, os_, gp, "nvfp4", wc, ws, 1.0, None, 1, 1024, 5120, 0, 1)] * threads,
+            32768 * n / 1024)
+    return out
+
+
 # ---------------------------------------------------------------- traffic from PMC runs
-def traffic_record(kernel_source: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, only if
-    they were taken from the current kernel source"""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def source_sha(kernel_source: str) -> str:
+    """SHA-256 of a kernel source and the headers it includes"""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp4_e4m3_amd", "csrc")
+    for name in (kernel_source, "nv_encode.hpp", "fp4q_internal.hpp"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel_source: str, name: str = "traffic.json"):
+    """a committed record from rocprofv3 --pmc runs (HBM bytes, MFMA busy),
+    only if it was taken from the current kernel source"""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "block_scaled_fp4_e4m3_amd", "csrc", kernel_source), "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != source_sha(kernel_source):
         return None
     return rec
 
@@ -661,29 +805,61 @@ def summarize_stats(stats_csv: str, out_md: str, title: str, command: str) -> No
                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |\n")
 
 
-def _counter_means(csv_path: str, counter: str, name_part: str):
+def _counter_means(csv_path: str, counter: str, name_part: str, largest_grid: bool = False):
+    """mean value of a counter over the dispatches of kernels matching
+    name_part (with largest_grid: only those with the largest grid, the
+    workload's own launches)"""
     import csv
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
-            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    rows = [r for r in csv.DictReader(open(csv_path)) if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if largest_grid and rows:
+        g = max(int(r["Grid_Size"]) for r in rows)
+        rows = [r for r in rows if int(r["Grid_Size"]) == g]
+    vals = [float(r["Counter_Value"]) for r in rows]
     if not vals:
         raise SystemExit(f"no {counter} samples for kernels matching {name_part!r} in {csv_path}")
     return float(np.mean(vals)), len(vals)
 
 
+def mfma_from_pmc(workload: str, csv_path: str, out_json: str, kernel: str = "gemm_tile_kernel",
+                  xcds: int = 8, simds: int = 1024) -> dict:
+    """MFMA busy fraction and shader clock of `kernel` from one rocprofv3 run
+    of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+    SQ_INSTS_VALU_MFMA_MOPS_F16 (the profiler's MfmaUtil: busy cycles summed
+    over the SIMDs over GUI-active cycles times the SIMD count; the reported
+    GRBM_GUI_ACTIVE is the sum over the XCDs)"""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatches of {kernel!r} in {csv_path}")
+    busy = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / xcds * simds) for d in per.values()]
+    clk = [d["GRBM_GUI_ACTIVE"] / xcds / d["dur_ns"] for d in per.values()]
+    flops = [d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512 for d in per.values()]
+    rec = {"workload": workload, "kernel": kernel, "source_sha256": source_sha("gemm.hip"),
+           "dispatches": len(per), "mfma_busy": float(np.mean(busy)), "sclk_GHz": float(np.mean(clk)),
+           "mfma_flops_per_launch": float(np.mean(flops))}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    return rec
+
+
 def traffic_from_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
-                     out_json: str, kernel: str = "gemm_tile_kernel") -> dict:
+                     out_json: str, kernel: str = "gemm_tile_kernel", source: str = "gemm.hip",
+                     largest_grid: bool = False) -> dict:
     """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the copy probe"""
-    fk, nf = _counter_means(fetch_csv, "FETCH_SIZE", kernel)
-    wk, nw = _counter_means(write_csv, "WRITE_SIZE", kernel)
+    fk, nf = _counter_means(fetch_csv, "FETCH_SIZE", kernel, largest_grid)
+    wk, nw = _counter_means(write_csv, "WRITE_SIZE", kernel, largest_grid)
     cf, _ = _counter_means(copy_fetch_csv, "FETCH_SIZE", "neg")
     cw, _ = _counter_means(copy_write_csv, "WRITE_SIZE", "neg")
     f_scale = cf * 1024.0 / COPY_PROBE_BYTES   # counter KiB per true KiB
     w_scale = cw * 1024.0 / COPY_PROBE_BYTES
     fetch_b = fk * 1024.0 / f_scale
     write_b = wk * 1024.0 / w_scale
-    src = open(os.path.join(ROOT, "block_scaled_fp4_e4m3_amd", "csrc", "gemm.hip"), "rb").read()
-    rec = {"workload": workload, "kernel": kernel, "source_sha256": hashlib.sha256(src).hexdigest(),
+    rec = {"workload": workload, "kernel": kernel, "source_sha256": source_sha(source),
            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
            "bytes_per_launch": fetch_b + write_b, "dispatches": {"fetch": nf, "write": nw},
            "copy_probe_scale": {"fetch": f_scale, "write": w_scale}}
@@ -701,6 +877,9 @@ def main():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other rows (MXFP4 linear, decode batch sizes, variants, MACaQ, search)")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-scaling copy kernel and exit")
+    ap.add_argument("--config-table", action="store_true",
+                    help="GPU and oracle (1 thread and all host threads) times of every workload's quantize and "
+                         "GEMM, one JSON line, exit")
     ap.add_argument("--quant-sweep", action="store_true",
                     help="time the NVFP4 quantizer over rules x block sizes on 4096 x 4096 FP32, print one JSON line, exit")
     ap.add_argument("--only", choices=["quantize", "gemm"],
@@ -708,6 +887,11 @@ def main():
                          "for rocprofv3 counter runs")
     ap.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--mfma-record", nargs=2, metavar=("PMC_CSV", "OUT_JSON"),
+                    help="MFMA busy fraction and clock of the GEMM of --workload from a rocprofv3 --pmc CSV, then exit")
+    ap.add_argument("--quant-traffic-record", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT_JSON"),
+                    help="HBM bytes per quantize launch of --workload from rocprofv3 --pmc CSVs, then exit")
     ap.add_argument("--traffic-record", nargs=5,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "OUT_JSON"),
                     help="HBM bytes per GEMM launch of --workload from rocprofv3 --pmc CSVs, then exit")
@@ -715,11 +899,19 @@ def main():
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
         return
+    wl_name = {"prefill": "prefill_hybrid_layer_M32768_K5120_N10240-17408-5120",
+               "mxfp4_linear": "mxfp4_linear_M4096_K4096_N14336",
+               "razer_decode": "razer_decode_M128_K5120_N17408"}[args.workload]
     if args.traffic_record:
-        wl_name = {"prefill": "prefill_hybrid_layer_M32768_K5120_N10240-17408-5120",
-                   "mxfp4_linear": "mxfp4_linear_M4096_K4096_N14336",
-                   "razer_decode": "razer_decode_M128_K5120_N17408"}[args.workload]
         print(json.dumps(traffic_from_pmc(wl_name, *args.traffic_record)))
+        return
+    if args.quant_traffic_record:
+        print(json.dumps(traffic_from_pmc(wl_name, *args.quant_traffic_record,
+                                          kernel=WORKLOADS[args.workload].quant_kernel, source="quantize.hip",
+                                          largest_grid=True)))
+        return
+    if args.mfma_record:
+        print(json.dumps(mfma_from_pmc(wl_name, *args.mfma_record, kernel=WORKLOADS[args.workload].gemm_kernel)))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -737,6 +929,9 @@ def main():
         return
     if args.quant_sweep:
         print(json.dumps(quant_sweep()))
+        return
+    if args.config_table:
+        print(json.dumps(config_table(B)))
         return
 
     wl = WORKLOADS[args.workload](B)
@@ -790,6 +985,13 @@ def main():
     roofline = {"bound": "mfma", "kernel": wl.gemm_kernel, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "avg_launch_ms": round(gemm_avg_ms, 4), "algorithmic_flops_per_launch": gemm_avg_flops}
+    mrec = traffic_record("gemm.hip", "mfma_busy.json")
+    if mrec and mrec.get("workload") == wl.config()["workload"]:
+        # counters of the same kernel: the MFMA pipes' busy fraction and the
+        # shader clock during it (the published peak assumes 2.4 GHz)
+        roofline.update({"mfma_busy": round(mrec["mfma_busy"], 4), "sclk_GHz": round(mrec["sclk_GHz"], 3)})
+    qrec = traffic_record("quantize.hip", "traffic_quantize.json")
+    q_traffic = qrec.get("bytes_per_launch") if qrec and qrec.get("workload") == wl.config()["workload"] else None
     quant_gbs = wl.quant_bytes / (q_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -806,7 +1008,7 @@ def main():
         "data": "synthetic",
         "config": wl.config(),
         "quantize": {"kernel": wl.quant_kernel, "avg_launch_ms": round(q_ms, 4), "timing": "graph replay",
-                     "step_interval_ms": round(q_interval_ms, 4), "bytes": wl.quant_bytes,
+                     "step_interval_ms": round(q_interval_ms, 4), "bytes": wl.quant_bytes, "traffic": q_traffic,
                      "GB/s": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4)},
         "gemm": [{"N": n, "avg_launch_ms": round(t, 4), "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1),
                   "frac": round(f / (t * 1e-3) / 1e12 / peak, 4)} for n, t, f in zip(wl.NS, g_ms, wl.gemm_flops)],
