@@ -231,30 +231,41 @@ __global__ __launch_bounds__(256) void macaq_refine_kernel(MacaqParams p, int64_
   }
   __syncthreads();
   if (!live) return;  // uniform per wave; no barrier follows
-  int64_t taken = 0;
-  while (taken < p.max_moves) {
-    double best = 0.0;
-    int64_t bidx = INT64_MAX;  // 2 k + (0 up, 1 down)
-    for (int64_t k = lane; k < K; k += 64) {
-      const int li = lv[k];
-      const double sc = ldexp(1.0, ex[k / 32]);
-      const double rk = r[k], hkk = diag[k];
-#pragma unroll
-      for (int dir = 0; dir < 2; ++dir) {
-        const int nl = dir == 0 ? li + 1 : li - 1;
-        if (nl < 0 || nl > 14) continue;
-        const double delta = (level_value(nl) - level_value(li)) * sc;
-        const double t1 = delta * rk;
-        const double t2 = delta * delta;
-        const double q = 2.0 * t1 + t2 * hkk;
-        const double gain = -q;
-        if (gain > best) {
-          best = gain;
-          bidx = 2 * k + dir;
-        }
+  // the gain of each one-level move of element j (up, then down; strict >
+  // keeps the first, so a tie keeps the smaller j, then up) into the lane's
+  // (best, bidx); the step between adjacent levels l and l + 1 is 2 for the
+  // outer pairs (-6/-4, 4/6), 1 for -4/-3, -3/-2, 2/3, 3/4 and 0.5 otherwise
+  double best = 0.0;
+  int64_t bidx = INT64_MAX;  // 2 j + (0 up, 1 down)
+  auto step_up = [](int l) -> double {
+    const int t = l >= 7 ? l - 7 : 6 - l;
+    return t < 4 ? 0.5 : (t < 6 ? 1.0 : 2.0);
+  };
+  auto consider = [&](int64_t j, double rj) {
+    const int li = lv[j];
+    const double sc = ldexp(1.0, ex[j / 32]);
+    const double hjj = diag[j];
+    if (li < 14) {
+      const double delta = step_up(li) * sc;
+      const double q = 2.0 * (delta * rj) + (delta * delta) * hjj;
+      const double gain = -q;
+      if (gain > best) {
+        best = gain;
+        bidx = 2 * j;
       }
     }
-    // the wave's best: largest gain, then the smaller index
+    if (li > 0) {
+      const double delta = -step_up(li - 1) * sc;
+      const double q = 2.0 * (delta * rj) + (delta * delta) * hjj;
+      const double gain = -q;
+      if (gain > best) {
+        best = gain;
+        bidx = 2 * j + 1;
+      }
+    }
+  };
+  // the wave's best: largest gain, then the smaller index
+  auto wave_best = [&]() {
 #pragma unroll
     for (int d = 1; d < 64; d *= 2) {
       const double og = shfl_xor_d(best, d);
@@ -265,17 +276,56 @@ __global__ __launch_bounds__(256) void macaq_refine_kernel(MacaqParams p, int64_
         bidx = oi;
       }
     }
-    if (!(best > 0.0)) break;  // no move gains: the row leaves the active set
+  };
+  for (int64_t k = lane; k < K; k += 64) consider(k, r[k]);
+  wave_best();
+  // Each move: r_j += delta * H[k][j] for every j, and the next move's gains
+  // from the updated r in the same pass.  Lane l owns j = l + 64 i; the row
+  // of H comes in groups of kGroup elements per lane, the next group's loads
+  // in flight while the current one is used.
+  constexpr int kGroup = 16;
+  const int64_t nper = (K + 63) / 64, ngroups = (nper + kGroup - 1) / kGroup;
+  int64_t taken = 0;
+  while (taken < p.max_moves && best > 0.0) {
     const int64_t k = bidx >> 1;
     const int li = lv[k];
     const int nl = (bidx & 1) ? li - 1 : li + 1;
-    const double delta = (level_value(nl) - level_value(li)) * ldexp(1.0, ex[k / 32]);
-    // the whole wave has read lv[k] (and the scan read every r) before the
-    // writes below; LDS operations of one wave complete in order
+    const double delta = ((bidx & 1) ? -step_up(nl) : step_up(li)) * ldexp(1.0, ex[k / 32]);
+    const double* hrow = p.h + k * p.ldh;
+    double cur[kGroup], nxt[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const int64_t j = lane + 64 * (int64_t)i;
+      cur[i] = j < K ? hrow[j] : 0.0;
+    }
+    // the whole wave has read lv[k] before the write; LDS operations of one
+    // wave complete in order, so the pass below sees the new level
     __builtin_amdgcn_wave_barrier();
     if (lane == (int)(k & 63)) lv[k] = (uint8_t)nl;
-    const double* hrow = p.h + k * p.ldh;
-    for (int64_t j = lane; j < K; j += 64) r[j] = r[j] + delta * hrow[j];
+    __builtin_amdgcn_wave_barrier();
+    best = 0.0;
+    bidx = INT64_MAX;
+    for (int64_t g = 0; g < ngroups; ++g) {
+      if (g + 1 < ngroups) {
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+          const int64_t j = lane + 64 * ((g + 1) * kGroup + i);
+          nxt[i] = j < K ? hrow[j] : 0.0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int64_t j = lane + 64 * (g * kGroup + i);
+        if (j < K) {
+          const double rj = r[j] + delta * cur[i];
+          r[j] = rj;
+          consider(j, rj);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) cur[i] = nxt[i];
+    }
+    wave_best();
     __builtin_amdgcn_wave_barrier();
     ++taken;
   }
