@@ -200,145 +200,140 @@ __global__ __launch_bounds__(256) void macaq_hd_kernel(MacaqParams p, int64_t n0
 }
 
 // ---------------------------------------------------------------- 3. refinement
-// One wave per row; the waves of a workgroup share the diagonal of H in LDS,
-// and each keeps its row's r (binary64), levels (0..14) and exponents in LDS.
-// Lane l scans elements k = l, l + 64, ... (k ascending, the move up before
-// the move down); the wave takes the largest gain (a tie keeps the smaller k,
-// then up) and adds delta * H[k][j] to every r_j.
+// One workgroup of four waves per row.  Wave w owns the elements
+// j = 64 (4 i + w) + lane (i = 0, 1, ...) and keeps their r (binary64), levels
+// and exponents in registers; the diagonal of H sits in LDS.  A move: every
+// lane adds delta * H[k][j] to its r_j and, in the same pass, forms the two
+// gains of each of its elements from the updated r (up before down; strict >
+// keeps the first, so a tie keeps the smaller j, then up); each wave takes its
+// best by a butterfly (largest gain, then the smaller index), and the four
+// wave bests meet in LDS under the same rule, so every thread knows the next
+// move.  The LDS slots alternate between two sets, one barrier per move.
 constexpr int kMacaqMaxK = 80 * 64;
-constexpr size_t kMacaqLds = 160 * 1024;
+constexpr int kRowWaves = 4;
+constexpr int kPer = kMacaqMaxK / (64 * kRowWaves);  // elements per lane, at most
 
-__host__ __device__ __forceinline__ size_t refine_wave_bytes(int64_t K) { return (size_t)K * 9 + (size_t)K / 32; }
+struct MoveBest {
+  double gain;
+  int64_t idx;  // 2 j + (0 up, 1 down); INT64_MAX: none
+  double delta;
+};
 
-__global__ __launch_bounds__(256) void macaq_refine_kernel(MacaqParams p, int64_t n0, int64_t rows, const double* R) {
-  extern __shared__ __align__(16) uint8_t lds[];
+__device__ __forceinline__ bool better(double g, int64_t i, double bg, int64_t bi) {
+  return g > bg || (g == bg && i < bi);
+}
+
+__global__ __launch_bounds__(64 * kRowWaves) void macaq_refine_kernel(MacaqParams p, int64_t n0, const double* R) {
+  __shared__ MoveBest slot[2][kRowWaves];
+  __shared__ double hd[kMacaqMaxK];
   const int64_t K = p.K;
-  const int waves = (int)(blockDim.x >> 6), wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  double* diag = (double*)lds;
-  double* r = (double*)(lds + (size_t)K * 8 + (size_t)wave * refine_wave_bytes(K));
-  uint8_t* lv = (uint8_t*)(r + K);
-  int8_t* ex = (int8_t*)(lv + K);
-  for (int64_t k = threadIdx.x; k < K; k += blockDim.x) diag[k] = p.h[k * p.ldh + k];
-  const int64_t nr = (int64_t)blockIdx.x * waves + wave;
-  const bool live = nr < rows;
-  const int64_t row = n0 + (live ? nr : 0);
-  if (live) {
-    for (int64_t k = lane; k < K; k += 64) {
-      r[k] = R[nr * K + k];
-      lv[k] = (uint8_t)level_of((p.codes[row * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu);
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t nr = blockIdx.x, row = n0 + nr;
+  double r[kPer];
+  int st[kPer];  // level (bits 3:0) and exponent + 128 (bits 15:4)
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t j = 64 * (kRowWaves * (int64_t)i + wave) + lane;
+    r[i] = 0.0;
+    st[i] = 7 | (128 << 4);
+    if (j < K) {
+      r[i] = R[nr * K + j];
+      hd[j] = p.h[j * p.ldh + j];
+      const int lv = level_of((p.codes[row * (K / 2) + j / 2] >> (4 * (j & 1))) & 0xFu);
+      const int e = (int)p.scales[row * (K / 32) + j / 32] - 127;
+      st[i] = lv | ((e + 128) << 4);
     }
-    for (int64_t b = lane; b < K / 32; b += 64) ex[b] = (int8_t)((int)p.scales[row * (K / 32) + b] - 127);
   }
-  __syncthreads();
-  if (!live) return;  // uniform per wave; no barrier follows
-  // the gain of each one-level move of element j (up, then down; strict >
-  // keeps the first, so a tie keeps the smaller j, then up) into the lane's
-  // (best, bidx); the step between adjacent levels l and l + 1 is 2 for the
-  // outer pairs (-6/-4, 4/6), 1 for -4/-3, -3/-2, 2/3, 3/4 and 0.5 otherwise
-  double best = 0.0;
-  int64_t bidx = INT64_MAX;  // 2 j + (0 up, 1 down)
+  // the step between adjacent levels l and l + 1 (l in 0..13): 2 for the
+  // outer pairs (-6/-4, 4/6), 1 for -4/-3, -3/-2, 2/3, 3/4, 0.5 otherwise
   auto step_up = [](int l) -> double {
     const int t = l >= 7 ? l - 7 : 6 - l;
     return t < 4 ? 0.5 : (t < 6 ? 1.0 : 2.0);
   };
-  auto consider = [&](int64_t j, double rj) {
-    const int li = lv[j];
-    const double sc = ldexp(1.0, ex[j / 32]);
-    const double hjj = diag[j];
+  MoveBest b{0.0, INT64_MAX, 0.0};
+  __syncthreads();  // the diagonal is in LDS
+  auto consider = [&](int i, int64_t j) {
+    const int li = st[i] & 15;
+    const double hjj = hd[j];
+    const double sc = ldexp(1.0, (st[i] >> 4) - 128);
     if (li < 14) {
       const double delta = step_up(li) * sc;
-      const double q = 2.0 * (delta * rj) + (delta * delta) * hjj;
+      const double q = 2.0 * (delta * r[i]) + (delta * delta) * hjj;
       const double gain = -q;
-      if (gain > best) {
-        best = gain;
-        bidx = 2 * j;
-      }
+      if (gain > b.gain) b = MoveBest{gain, 2 * j, delta};
     }
     if (li > 0) {
       const double delta = -step_up(li - 1) * sc;
-      const double q = 2.0 * (delta * rj) + (delta * delta) * hjj;
+      const double q = 2.0 * (delta * r[i]) + (delta * delta) * hjj;
       const double gain = -q;
-      if (gain > best) {
-        best = gain;
-        bidx = 2 * j + 1;
-      }
+      if (gain > b.gain) b = MoveBest{gain, 2 * j + 1, delta};
     }
   };
-  // the wave's best: largest gain, then the smaller index
-  auto wave_best = [&]() {
+  // the row's best: a butterfly per wave, then the four waves through LDS
+  auto row_best = [&](int par) {
 #pragma unroll
     for (int d = 1; d < 64; d *= 2) {
-      const double og = shfl_xor_d(best, d);
-      const int64_t oi = (int64_t)(((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)((uint64_t)bidx >> 32), d) << 32) |
-                                   (uint32_t)__shfl_xor((int)(uint32_t)bidx, d));
-      if (og > best || (og == best && oi < bidx)) {
-        best = og;
-        bidx = oi;
-      }
+      const double og = shfl_xor_d(b.gain, d), od = shfl_xor_d(b.delta, d);
+      const int64_t oi = (int64_t)(((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)((uint64_t)b.idx >> 32), d) << 32) |
+                                   (uint32_t)__shfl_xor((int)(uint32_t)b.idx, d));
+      if (better(og, oi, b.gain, b.idx)) b = MoveBest{og, oi, od};
     }
+    if (lane == 0) slot[par][wave] = b;
+    __syncthreads();
+    MoveBest g = slot[par][0];
+#pragma unroll
+    for (int w = 1; w < kRowWaves; ++w) {
+      const MoveBest o = slot[par][w];
+      if (better(o.gain, o.idx, g.gain, g.idx)) g = o;
+    }
+    b = g;
   };
-  for (int64_t k = lane; k < K; k += 64) consider(k, r[k]);
-  wave_best();
-  // Each move: r_j += delta * H[k][j] for every j, and the next move's gains
-  // from the updated r in the same pass.  Lane l owns j = l + 64 i; the row
-  // of H comes in groups of kGroup elements per lane, the next group's loads
-  // in flight while the current one is used.
-  constexpr int kGroup = 16;
-  const int64_t nper = (K + 63) / 64, ngroups = (nper + kGroup - 1) / kGroup;
-  int64_t taken = 0;
-  while (taken < p.max_moves && best > 0.0) {
-    const int64_t k = bidx >> 1;
-    const int li = lv[k];
-    const int nl = (bidx & 1) ? li - 1 : li + 1;
-    const double delta = ((bidx & 1) ? -step_up(nl) : step_up(li)) * ldexp(1.0, ex[k / 32]);
-    const double* hrow = p.h + k * p.ldh;
-    double cur[kGroup], nxt[kGroup];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const int64_t j = lane + 64 * (int64_t)i;
-      cur[i] = j < K ? hrow[j] : 0.0;
-    }
-    // the whole wave has read lv[k] before the write; LDS operations of one
-    // wave complete in order, so the pass below sees the new level
-    __builtin_amdgcn_wave_barrier();
-    if (lane == (int)(k & 63)) lv[k] = (uint8_t)nl;
-    __builtin_amdgcn_wave_barrier();
-    best = 0.0;
-    bidx = INT64_MAX;
-    for (int64_t g = 0; g < ngroups; ++g) {
-      if (g + 1 < ngroups) {
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          const int64_t j = lane + 64 * ((g + 1) * kGroup + i);
-          nxt[i] = j < K ? hrow[j] : 0.0;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int64_t j = lane + 64 * (g * kGroup + i);
-        if (j < K) {
-          const double rj = r[j] + delta * cur[i];
-          r[j] = rj;
-          consider(j, rj);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) cur[i] = nxt[i];
-    }
-    wave_best();
-    __builtin_amdgcn_wave_barrier();
-    ++taken;
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t j = 64 * (kRowWaves * (int64_t)i + wave) + lane;
+    if (j < K) consider(i, j);
   }
-  if (p.moves && lane == 0) p.moves[row] = (int32_t)taken;
-  __builtin_amdgcn_wave_barrier();
-  for (int64_t m = lane; m < K / 2; m += 64)
-    p.codes[row * (K / 2) + m] = (uint8_t)(code_of(lv[2 * m]) | (code_of(lv[2 * m + 1]) << 4));
-}
-
-int refine_waves(int64_t K) {
-  for (int w = 4; w > 1; --w)
-    if ((size_t)K * 8 + (size_t)w * refine_wave_bytes(K) <= kMacaqLds) return w;
-  return 1;
+  row_best(0);
+  int64_t taken = 0;
+  while (taken < p.max_moves && b.gain > 0.0) {
+    const int64_t k = b.idx >> 1;
+    const bool down = (b.idx & 1) != 0;
+    const double delta = b.delta;
+    const double* hrow = p.h + k * p.ldh;
+    double hv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t j = 64 * (kRowWaves * (int64_t)i + wave) + lane;
+      hv[i] = j < K ? hrow[j] : 0.0;
+    }
+    // the moved element's new level, in its owner's registers
+    if (wave == (int)((k >> 6) % kRowWaves) && lane == (int)(k & 63)) {
+      const int ki = (int)(k >> 8);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (i == ki) st[i] += down ? -1 : 1;
+    }
+    b = MoveBest{0.0, INT64_MAX, 0.0};
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t j = 64 * (kRowWaves * (int64_t)i + wave) + lane;
+      if (j < K) {
+        r[i] = r[i] + delta * hv[i];
+        consider(i, j);
+      }
+    }
+    ++taken;
+    row_best((int)(taken & 1));
+  }
+  if (p.moves && threadIdx.x == 0) p.moves[row] = (int32_t)taken;
+  // codes: element j (even lane) and j + 1 (the next lane) share a byte
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t j = 64 * (kRowWaves * (int64_t)i + wave) + lane;
+    const uint32_t c = code_of(st[i] & 15);
+    const uint32_t hi = (uint32_t)__shfl_down((int)c, 1);
+    if (j < K && (lane & 1) == 0) p.codes[row * (K / 2) + j / 2] = (uint8_t)(c | (hi << 4));
+  }
 }
 
 }  // namespace
@@ -353,17 +348,11 @@ hipError_t launch_macaq(const MacaqParams& p, void* workspace, size_t ws_bytes, 
   if (e != hipSuccess) return e;
   const int64_t chunk = std::min<int64_t>(p.N, (int64_t)(ws_bytes / ((size_t)p.K * sizeof(double))));
   double* R = (double*)workspace;
-  const int waves = refine_waves(p.K);
-  const size_t lds = (size_t)p.K * 8 + (size_t)waves * refine_wave_bytes(p.K);
-  // the refinement's LDS can exceed the default limit of a launch
-  e = hipFuncSetAttribute((const void*)macaq_refine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMacaqLds);
-  if (e != hipSuccess) return e;
   for (int64_t n0 = 0; n0 < p.N; n0 += chunk) {
     const int64_t rows = std::min(chunk, p.N - n0);
     const dim3 g((unsigned)((p.K + kHdTile - 1) / kHdTile), (unsigned)((rows + kHdTile - 1) / kHdTile));
     hipLaunchKernelGGL(macaq_hd_kernel, g, dim3(256), 0, s, p, n0, rows, R);
-    hipLaunchKernelGGL(macaq_refine_kernel, dim3((unsigned)((rows + waves - 1) / waves)), dim3(64 * waves), lds, s, p,
-                       n0, rows, (const double*)R);
+    hipLaunchKernelGGL(macaq_refine_kernel, dim3((unsigned)rows), dim3(64 * kRowWaves), 0, s, p, n0, (const double*)R);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
