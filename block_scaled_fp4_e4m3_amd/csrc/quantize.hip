@@ -512,6 +512,239 @@ __global__ __launch_bounds__(kThreads) void nv16_kernel(QuantParams p) {
   }
 }
 
+// ---------------------------------------------------------------- NVFP4 4-over-6, decided from estimates
+// 4-over-6 ("Finer is Better", Method 2) keeps the scale whose FP32 block
+// error is lower.  nv16_kernel forms both candidates' exact codes (two
+// bracketed converts each) and both exact errors.  Here each candidate is
+// encoded once, at y = x * rlo (rlo just below 1/(s g)), and its error is
+// estimated in units of s g as S = sum (y - v(y))^2, where v(y) is the value
+// of y's code.  Only the chosen candidate's codes get the upper bracket.
+//
+// Why the estimate decides exactly.  Let t = x / (s g) and v(t) its exact
+// E2M1 code value; the oracle's error is E = (s g)^2 T (1 + th) with
+// T = sum (t - v(t))^2 and |th| < 8 u (u = 2^-24: one rounding of e, one of
+// e^2, a tree of depth 4).  |y - t| <= |t| 1.32 2^-20 (the bracket factor,
+// the reciprocal's ulp and three roundings), so with y_max = a * rlo every
+// element has |y - t| <= dl = 1.5 2^-20 y_max.  Both v are nearest values,
+// so ||y - v(y)| - |t - v(t)|| <= dl, and by Cauchy-Schwarz over 16 terms
+// |S - T| <= 8 dl sqrt(S) + 16 dl^2 (plus the sum's own roundings, below
+// 12 u relative).  P = s^2 S and Q = s^2 (that bound) then give: E4 < E6
+// surely when P4 + Q4 + rho < P6 - Q6, and E4 > E6 surely when
+// P4 - Q4 > P6 + Q6 + rho, with rho = 2^-17 (P4 + P6) covering every other
+// rounding.  The codes of y at an element that sits on a midpoint may be
+// either neighbour; both are dl-close in error, which the bound covers.
+// Ranges that keep every step normal and finite (s g in [2^-50, 2^50],
+// y_max < 64, a finite error) are required as well; a lane outside them, or
+// whose estimates are too close, takes the exact 4-over-6 of nv16_kernel.
+
+struct Four6Block {
+  uint32_t lo, hi;  // codes of elements 0-7 and 8-15
+  int sbyte;
+};
+
+// the exact 4-over-6 of one 16-element NVFP4 block (nv16_kernel's steps)
+__device__ __attribute__((noinline)) Four6Block four6_exact16(float __attribute__((ext_vector_type(16))) xv,
+                                                               float g, int pz) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = xv[i];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, fbits(x[i]) & 0x7FFFFFFFu);
+  const bool finite = amax < 0x7F800000u;
+  const double gd = (double)g;
+  int k6 = select_sf_exact<0>(bitsf(amax), 1.0 / (6.0 * gd), 6.0 * gd);
+  int k4 = select_sf_exact<0>(bitsf(amax), 1.0 / (4.0 * gd), 4.0 * gd);
+  if (pz && k6 == 0) k6 = 1;
+  if (pz && k4 == 0) k4 = 1;
+  const float s6 = e4m3_f32(k6), s4 = e4m3_f32(k4);
+  const uint2 c6 = encode_nv16<1, 0>(x, k6, s6, g, finite);
+  const uint2 c4 = encode_nv16<1, 0>(x, k4, s4, g, finite);
+  const float e6 = lane_sse16(x, c6, s6, g);
+  const float e4 = lane_sse16(x, c4, s4, g);
+  Four6Block o;
+  if (e4 < e6) { o.lo = c4.x; o.hi = c4.y; o.sbyte = k4; }
+  else { o.lo = c6.x; o.hi = c6.y; o.sbyte = k6; }
+  return o;
+}
+
+// max(|a|, |b|, |c|) in one instruction (the compiler would first quiet each
+// input); a NaN input is dropped, and its block then fails the finite-error
+// test below
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// one candidate: codes of y = x * rl (elements 0-7, 8-15) and
+// S = sum (y - v(y))^2 as two FMA chains
+__device__ __forceinline__ float four6_candidate(const float* x, float rl, uint32_t& ca, uint32_t& cb) {
+  float y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = x[i] * rl;
+  ca = 0;
+  cb = 0;
+  static_for<0, 4>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    ca = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ca, y[2 * b], y[2 * b + 1], 1.0f, b);
+    cb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cb, y[8 + 2 * b], y[9 + 2 * b], 1.0f, b);
+  });
+  float sa = 0.0f, sb = 0.0f;
+  static_for<0, 4>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    const auto va = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ca, 1.0f, b);
+    const auto vb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cb, 1.0f, b);
+    const float d0 = y[2 * b] - va[0], d1 = y[2 * b + 1] - va[1];
+    const float d2 = y[8 + 2 * b] - vb[0], d3 = y[9 + 2 * b] - vb[1];
+    sa = __builtin_fmaf(d0, d0, sa);
+    sb = __builtin_fmaf(d2, d2, sb);
+    sa = __builtin_fmaf(d1, d1, sa);
+    sb = __builtin_fmaf(d3, d3, sb);
+  });
+  return sa + sb;
+}
+
+// Codes of a lane's 16 elements whose two bracketed codes differ (the exact
+// code is the low one or one magnitude step above).  The element is past its
+// midpoint Q g (Q = midpoint * s, exact) by the sign of fma(-Q, g, |x|), a
+// single rounding of the exact difference, which lies far from the underflow
+// range for s g in [2^-50, 2^50]; a tie rounds up from an odd magnitude (to
+// the even one).  The 16 positions are visited in order, each only when some
+// lane of the wave has it ambiguous: every element is named by a constant
+// index (an element chosen by a run-time index would put the elements in
+// memory), and nothing is called (a call waits for the loads in flight).
+__device__ __forceinline__ void resolve16(const float* x, uint32_t& wa, uint32_t& wb, uint32_t ha, uint32_t hb,
+                                          float s, float g) {
+  const uint32_t aa = wa ^ ha, ab = wb ^ hb;
+  static_for<0, 16>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int sh = 4 * (i & 7);
+    const uint32_t am = (i < 8 ? aa : ab) & (0xFu << sh);
+    if (!wave_all(am == 0)) {
+      uint32_t& w = i < 8 ? wa : wb;
+      const uint32_t mag = (w >> sh) & 7u;
+      typedef float f2v __attribute__((ext_vector_type(2)));
+      const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(mag | ((mag + 1u) << 4), 0.5f, 0);
+      const float Q = (v[0] + v[1]) * s;  // exact: at most 8 significant bits
+      const float e = __builtin_fmaf(-Q, g, fabsf(x[i]));
+      const bool go = am != 0 && mag != 7u && (e > 0.0f || (e == 0.0f && (mag & 1u) != 0));
+      w += go ? (1u << sh) : 0u;  // magnitude + 1 (at most 7: no carry)
+    }
+  });
+}
+
+// NVFP4, blocks of 16, rule 4-over-6, contiguous rows, optional
+// block-Hadamard of 16 (HAD = 0 or 16); same walk as nv16_kernel
+template <bool BF16, int HAD>
+__global__ __launch_bounds__(kThreads) void nv16_four6_kernel(QuantParams p) {
+  constexpr int L = 16;
+  const float g = p.global ? *p.global : 1.0f;
+  const int pz = p.prevent_zero;
+  const int64_t total = p.rows * (p.cols / L);
+  const bool gok = g > 0x1p-100f && g < 0x1p100f;
+  // scale codes by the hardware FP32 -> E4M3 convert bracketed on both sides
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * g), r4 = __builtin_amdgcn_rcpf(4.0f * g);
+  const float lo6 = r6 * (1.0f - 0x1p-20f), hi6 = r6 * (1.0f + 0x1p-20f);
+  const float lo4 = r4 * (1.0f - 0x1p-20f), hi4 = r4 * (1.0f + 0x1p-20f);
+  const float ag = __builtin_amdgcn_rcpf(g) * (1.0f + 0x1p-20f);  // above 1 / g
+
+  constexpr int U = 2;
+  const int lane = threadIdx.x & 63;
+  const int64_t pass = (int64_t)gridDim.x * kThreads;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); c0 < total; c0 += U * pass) {
+    Raw<L, BF16> raw[U];
+    int64_t cu[U];
+    bool vu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * pass + lane;
+      vu[u] = c < total;
+      cu[u] = vu[u] ? c : total - 1;
+      if (c0 + u * pass < total) load_raw<L, BF16>(p, 0, cu[u] * L, raw[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * pass >= total) break;
+      float x[L];
+      finish_chunk<L, BF16, false>(p, cu[u] * L, raw[u], x, false, HAD);
+      float a = max3_abs(x[0], x[1], x[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) a = max3_abs(a, x[i], x[i + 1]);
+      a = max3_abs(a, x[15], x[15]);
+
+      typedef short s2v __attribute__((ext_vector_type(2)));
+      const s2v z = {0, 0};
+      const s2v clo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * lo6, a * lo4, 1.0f, false);
+      const s2v chi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a * hi6, a * hi4, 1.0f, false);
+      const uint32_t wl = (uint16_t)clo[0], wh = (uint16_t)chi[0];
+      // codes past 126 (the NaN code, above 464) stand for the saturated 126;
+      // where the two ends differ, a / (T g) lies on or next to a scale
+      // midpoint (calibrated global scales make exact midpoints common), and
+      // one exact midpoint test settles it
+      int k6 = min((int)(wl & 0xFFu), 126), k4 = min((int)(wl >> 8), 126);
+      const bool m6 = k6 != min((int)(wh & 0xFFu), 126), m4 = k4 != min((int)(wh >> 8), 126);
+      if (!wave_all(!gok || !(m6 || m4))) {
+        if (gok && m6) k6 = e4m3_from_low(k6, a, 6.0f, g);
+        if (gok && m4) k4 = e4m3_from_low(k4, a, 4.0f, g);
+      }
+      bool valid = gok;
+      if (pz) { k6 = max(k6, 1); k4 = max(k4, 1); }
+      valid = valid && k6 > 0;  // k4 >= k6
+      const float s6 = e4m3_f32(k6), s4 = e4m3_f32(k4);
+      const float sg6 = s6 * g, sg4 = s4 * g;
+      valid = valid && sg6 >= 0x1p-50f && sg4 <= 0x1p50f;  // s6 <= s4
+      const float q6 = __builtin_amdgcn_rcpf(sg6), q4 = __builtin_amdgcn_rcpf(sg4);
+      const float rl6 = q6 * (1.0f - 0x1p-20f), rl4 = q4 * (1.0f - 0x1p-20f);
+
+      uint32_t c6a, c6b, c4a, c4b;
+      const float S6 = four6_candidate(x, rl6, c6a, c6b);
+      const float S4 = four6_candidate(x, rl4, c4a, c4b);
+      // the combined bound: s^2 dl sqrt(S) = 1.5 2^-20 (a / g) sqrt(P) (a / g
+      // rounded up through ag), the dl^2 and absolute terms below 2^-31 (a / g)^2
+      // (s <= a / (2 g) for both candidates)
+      const float P6 = (s6 * s6) * S6, P4 = (s4 * s4) * S4;  // s^2 exact: at most 8 significant bits
+      const float A = a * ag;
+      const float M = 0x1.9p-17f * A * (__builtin_amdgcn_sqrtf(P4) + __builtin_amdgcn_sqrtf(P6)) +
+                      0x1p-31f * (A * A) + 0x1p-17f * (P4 + P6);
+      valid = valid && a * rl6 < 64.0f && P4 + P6 < 0x1p100f;  // rl4 <= rl6
+      const bool pick4 = valid && k4 != k6 && P4 + M < P6;
+      const bool pick6 = valid && (k4 == k6 || P4 > P6 + M);
+      const bool dec = pick4 || pick6;
+
+      uint32_t wa = pick4 ? c4a : c6a, wb = pick4 ? c4b : c6b;
+      int sbyte = pick4 ? k4 : k6;
+      // the chosen codes at the upper end of the bracket
+      const float rh = (pick4 ? q4 : q6) * (1.0f + 0x1p-20f);
+      uint32_t ha = 0, hb = 0;
+      static_for<0, 4>([&](auto ic) {
+        constexpr int b = decltype(ic)::value;
+        ha = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ha, x[2 * b] * rh, x[2 * b + 1] * rh, 1.0f, b);
+        hb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hb, x[8 + 2 * b] * rh, x[9 + 2 * b] * rh, 1.0f, b);
+      });
+      if (!dec) { ha = wa; hb = wb; }
+      if (!wave_all(ha == wa && hb == wb)) resolve16(x, wa, wb, ha, hb, pick4 ? s4 : s6, g);
+      if (!wave_all(dec)) {
+        if (!dec) {
+          typedef float f16v __attribute__((ext_vector_type(16)));
+          f16v xv;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xv[i] = x[i];
+          const Four6Block o = four6_exact16(xv, g, pz);
+          wa = o.lo;
+          wb = o.hi;
+          sbyte = o.sbyte;
+        }
+      }
+      if (vu[u]) {
+        *(uint2*)(p.codes + cu[u] * (L / 2)) = make_uint2(clear_neg_zero(wa), clear_neg_zero(wb));
+        p.scales[cu[u]] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- MXFP4, 32 elements per lane
 // One lane owns a 32-element run: one MXFP4 block and one Hadamard group, so
 // the rotation runs in registers and the block maximum needs no exchange.
@@ -1137,6 +1370,18 @@ hipError_t launch_q3(bool bf16, const QuantParams& p, hipStream_t s) {
     if (contig && p.fused_denom == 0.0f) {
       // two runs per thread and iteration: at least one whole iteration each
       const int g16 = grid_for((p.rows * (p.cols / 16) + 1) / 2);
+      if constexpr (FMT == NVFP4 && B == 16 && RULE == FOUR6) {
+        if (p.hadamard == 0 || p.hadamard == 16) {
+          if (p.hadamard == 16) {
+            if (bf16) hipLaunchKernelGGL((nv16_four6_kernel<true, 16>), dim3(g16), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((nv16_four6_kernel<false, 16>), dim3(g16), dim3(kThreads), 0, s, p);
+          } else {
+            if (bf16) hipLaunchKernelGGL((nv16_four6_kernel<true, 0>), dim3(g16), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((nv16_four6_kernel<false, 0>), dim3(g16), dim3(kThreads), 0, s, p);
+          }
+          return hipGetLastError();
+        }
+      }
       if (bf16) hipLaunchKernelGGL((nv16_kernel<FMT, B, RULE, true>), dim3(g16), dim3(kThreads), 0, s, p);
       else hipLaunchKernelGGL((nv16_kernel<FMT, B, RULE, false>), dim3(g16), dim3(kThreads), 0, s, p);
       return hipGetLastError();
