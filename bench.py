@@ -57,7 +57,7 @@ class Prefill:
     M, K, NS = 32768, 5120, (10240, 17408, 5120)
     compute_dtype = "f16"
     gemm_kernel = "gemm_tile_kernel"
-    quant_kernel = "nv16_kernel"
+    quant_kernel = "nv16_four6_kernel"
 
     def __init__(self, B):
         import torch

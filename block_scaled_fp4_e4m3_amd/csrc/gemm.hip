@@ -1824,6 +1824,200 @@ __global__ __launch_bounds__(64 * SmCfg<MR>::WAVES, (MR == 1 ? (AM >= AM_Q_ABSMA
   });
 }
 
+// ---------------------------------------------------------------- M = 1: matrix-vector product
+// One activation row against N weight rows.  A matrix-core tile would use one
+// of its 32 rows, and its operand layout reads 16 bytes from each of 32 rows
+// per load; here a wave owns whole weight rows and lane l the 16-element
+// blocks l, l + 64, ..., so every load instruction reads 512 consecutive code
+// bytes (8 per lane) or 64 consecutive scale bytes, and reads past the row
+// end return zeros (buffer range).  Elements decode to their E2M1 values in
+// f16 (RaZeR's code 0x8 to its special value), exactly; a block's 16
+// products meet in v_dot2_f32_f16, exactly (values are multiples of 1/2 of
+// at most 8, so every partial sum is a multiple of 1/4 below 2^11), and the
+// block sum is then multiplied by the product of the two block scales (at
+// most 8 significant bits, exact) into the FP32 sum.  The activation's blocks
+// are decoded once per wave.  Each wave keeps two rows' loads in flight
+// (fixed ping-pong registers, so no loop-carried moves wait on them); a row
+// past N gets a buffer view of no bytes, so its loads are issued but fetch
+// nothing.  The lane sums meet in a butterfly and lane 0 writes RN32(g * sum).
+constexpr int kGemvWaves = 4096;  // waves per launch (at most), several rows each
+
+// E2M1 values of 8 codes as f16, RaZeR's code 0x8 as the special value sp
+// (f16 in both halves of sp2): the convert gives -0 there, and a second
+// convert of a word with +1.0 exactly at those codes, times sp, is added
+template <int F>
+__device__ __forceinline__ half8 gemv_values8(uint32_t codes, uint32_t sp2) {
+  uint32_t t = 0;
+  if constexpr (F == RAZER_A || F == RAZER_W) {
+    const uint32_t y = codes ^ 0x88888888u;                     // nibble 0 where the code is 0x8
+    const uint32_t nz = ((y & 0x77777777u) + 0x77777777u) | y;  // bit 3: nibble != 0
+    t = (~nz & 0x88888888u) >> 2;                               // 0x2 (+1.0) where the code is 0x8
+  }
+  half8 out;
+  static_for<0, 4>([&](auto ic) {
+    constexpr int b = decltype(ic)::value;
+    half2v v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, b);
+    if constexpr (F == RAZER_A || F == RAZER_W) {
+      const half2v u = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(t, 1.0f, b);
+      v = __builtin_elementwise_fma(u, __builtin_bit_cast(half2v, sp2), v);
+    }
+    out[2 * b] = v[0];
+    out[2 * b + 1] = v[1];
+  });
+  return out;
+}
+
+// a block's scale as FP32 and its special value (f16, both halves)
+template <int F>
+__device__ __forceinline__ float gemv_scale(uint32_t sb, uint32_t sp_lo, uint32_t sp_hi, uint32_t& sp2) {
+  if constexpr (F == RAZER_W) {
+    const uint32_t i = (sb >> 6) & 3u;
+    sp2 = __builtin_amdgcn_perm(sp_hi, sp_lo, (2u * i) | ((2u * i + 1u) << 8) | ((2u * i) << 16) | ((2u * i + 1u) << 24));
+    return e3m3_f32(sb & 0x3Fu);
+  } else {
+    if constexpr (F == RAZER_A) sp2 = (sb & 0x80u) ? 0xC500C500u : 0x45004500u;  // -5 or +5
+    return __builtin_amdgcn_cvt_scalef32_f32_fp8(sb & 0x7Fu, 1.0f, 0);
+  }
+}
+
+// sum of the 16 products of a block (exact)
+__device__ __forceinline__ float dot16(const half8& a0, const half8& a1, const half8& w0, const half8& w1) {
+  const uint4 ua0 = __builtin_bit_cast(uint4, a0), ua1 = __builtin_bit_cast(uint4, a1);
+  const uint4 uw0 = __builtin_bit_cast(uint4, w0), uw1 = __builtin_bit_cast(uint4, w1);
+  float acc = 0.0f;
+  static_for<0, 4>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, u4_get(ua0, i)), __builtin_bit_cast(half2v, u4_get(uw0, i)),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, u4_get(ua1, i)), __builtin_bit_cast(half2v, u4_get(uw1, i)),
+                                 acc, false);
+  });
+  return acc;
+}
+
+template <int JB>
+struct GemvRow {
+  uint2 c[JB];
+  uint32_t sb[JB];
+};
+
+template <int JB>
+__device__ __forceinline__ void gemv_load(const GemmParams& p, int64_t n, int lane, GemvRow<JB>& r) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const int rowbytes = (int)(p.K / 2), nblk = (int)(p.K / 16);
+  const bool live = n < p.N;
+  const int64_t nn = live ? n : 0;
+  const auto wc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + nn * rowbytes), (short)0,
+                                                    live ? rowbytes : 0, (int)kRsrcWord3);
+  const auto ws = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_scales + nn * nblk), (short)0, live ? nblk : 0,
+                                                    (int)kRsrcWord3);
+  static_for<0, JB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wc, (lane + 64 * j) * 8, 0, 0);
+    r.c[j] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+    r.sb[j] = __builtin_amdgcn_raw_buffer_load_b8(ws, lane + 64 * j, 0, 0);
+  });
+}
+
+template <int FW, int JB>
+__device__ __forceinline__ void gemv_row(const GemmParams& p, int64_t n, int lane, const GemvRow<JB>& r,
+                                         const half8 (&a0)[JB], const half8 (&a1)[JB], const float (&sa)[JB],
+                                         uint32_t sp_lo, uint32_t sp_hi, float ga, float gw0) {
+  float acc[2] = {0.0f, 0.0f};
+  static_for<0, JB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    uint32_t sp2 = 0;
+    const float sw = gemv_scale<FW>(r.sb[j], sp_lo, sp_hi, sp2);
+    const half8 w0 = gemv_values8<FW>(r.c[j].x, sp2), w1 = gemv_values8<FW>(r.c[j].y, sp2);
+    acc[j & 1] = __builtin_fmaf(dot16(a0[j], a1[j], w0, w1), sa[j] * sw, acc[j & 1]);
+  });
+  float v = acc[0] + acc[1];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  if (lane == 0 && n < p.N) {
+    const float out = ga * col_w_global(p, gw0, n) * v;
+    if (p.c_bf16) {
+      uint32_t u = __float_as_uint(out);
+      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+      ((uint16_t*)p.c)[n] = (uint16_t)u;
+    } else {
+      ((float*)p.c)[n] = out;
+    }
+  }
+}
+
+template <int FA, int FW, int JB>
+__global__ __launch_bounds__(256) void gemv_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
+  const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+  // the first weight row's loads go out before the activation's
+  int64_t n = wave;
+  GemvRow<JB> rx, ry;
+  gemv_load<JB>(p, n, lane, rx);
+
+  half8 a0[JB], a1[JB];
+  float sa[JB];
+  {
+    const int rowbytes = (int)(p.K / 2), nblk = (int)(p.K / 16);
+    const auto ac = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_codes, (short)0, rowbytes, (int)kRsrcWord3);
+    const auto as = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_scales, (short)0, nblk, (int)kRsrcWord3);
+    GemvRow<JB> ra;
+    static_for<0, JB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ac, (lane + 64 * j) * 8, 0, 0);
+      ra.c[j] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+      ra.sb[j] = __builtin_amdgcn_raw_buffer_load_b8(as, lane + 64 * j, 0, 0);
+    });
+    static_for<0, JB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      uint32_t sp2 = 0;
+      sa[j] = gemv_scale<FA>(ra.sb[j], sp_lo, sp_hi, sp2);
+      a0[j] = gemv_values8<FA>(ra.c[j].x, sp2);
+      a1[j] = gemv_values8<FA>(ra.c[j].y, sp2);
+    });
+  }
+  const float ga = p.a_global ? *p.a_global : 1.0f;
+  const float gw0 = p.w_global ? *p.w_global : 1.0f;
+
+  while (true) {
+    gemv_load<JB>(p, n + nwaves, lane, ry);
+    gemv_row<FW, JB>(p, n, lane, rx, a0, a1, sa, sp_lo, sp_hi, ga, gw0);
+    n += nwaves;
+    if (n >= p.N) break;
+    gemv_load<JB>(p, n + nwaves, lane, rx);
+    gemv_row<FW, JB>(p, n, lane, ry, a0, a1, sa, sp_lo, sp_hi, ga, gw0);
+    n += nwaves;
+    if (n >= p.N) break;
+  }
+}
+
+// blocks per lane of the matrix-vector kernel for K, 0 if it does not apply
+int gemv_jb(const GemmParams& p) {
+  const uintptr_t a = (uintptr_t)p.a_codes | (uintptr_t)p.w_codes;
+  if (p.M != 1 || p.K % 16 != 0 || (a & 7u) != 0 || p.K > 64 * 16 * 8) return 0;
+  const int64_t per = (p.K / 16 + 63) / 64;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 3 ? 3 : per <= 5 ? 5 : 8;
+}
+
+template <int FA, int FW>
+hipError_t launch_gemv(const GemmParams& p, int jb, hipStream_t s) {
+  const int64_t waves = std::min<int64_t>(p.N, kGemvWaves);
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  switch (jb) {
+    case 1: hipLaunchKernelGGL((gemv_kernel<FA, FW, 1>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<FA, FW, 2>), grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<FA, FW, 3>), grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((gemv_kernel<FA, FW, 5>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((gemv_kernel<FA, FW, 8>), grid, block, 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
 int sm_blocks(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
 int sm_win(int mr) { return mr == 1 ? SmCfg<1>::WIN : mr == 2 ? SmCfg<2>::WIN : SmCfg<4>::WIN; }
 
@@ -1896,6 +2090,7 @@ hipError_t launch_small_m(const GemmParams& p, hipStream_t s, const Workspace& w
 
 template <int FA, int FW>
 hipError_t launch_nv(const GemmParams& p, hipStream_t s, const Workspace& ws) {
+  if (const int jb = gemv_jb(p)) return launch_gemv<FA, FW>(p, jb, s);
   if (small_m_fits(p)) return launch_small_m<FA, FW>(p, s, ws);
   return launch_tile<FA, FW>(p, s, ws);
 }

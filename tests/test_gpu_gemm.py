@@ -364,3 +364,44 @@ def test_gemm_fp32_split_k_is_deterministic(B, fa, fw, M, N, K):
         outs.append(host(out).view(np.uint32).copy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     assert np.all(np.isfinite(outs[0].view(np.float32)))  # every entry written
+
+
+# M = 1 (the matrix-vector kernel): K from one block to 8192 (1, 2, 3, 5 and 8
+# blocks per lane, ragged block counts that leave lanes past the row end), N
+# from one row to more rows than the launch has waves, every format pair of
+# the NVFP4 family, both output types; and K past the kernel's limit
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w"), ("razer_a", "nvfp4"),
+                                   ("nvfp4", "razer_a")])
+@pytest.mark.parametrize("N,K", [(1, 16), (33, 272), (300, 1040), (129, 2064), (70, 3072), (5000, 5120),
+                                 (64, 8192), (40, 8208)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_single_row(B, fa, fw, N, K, out_dtype):
+    a = datagen.student_t((1, K), 900 + K, 4.0)
+    w = datagen.normal((N, K), 910 + N, 0.02)
+    sp = SPECIAL if fw == "razer_w" else None
+    ca, sa, ga = oquant(a, fa)
+    cw, sw, gw = oquant(w, fw, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, 1, N, K)
+    case(f"gemm single row {fa}x{fw} 1x{N}x{K} {out_dtype}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp, out_dtype)
+    check(got, ref, out_dtype)
+
+
+@pytest.mark.parametrize("fa,fw", [("nvfp4", "nvfp4"), ("razer_a", "razer_w")])
+def test_gemm_single_row_exact_regime_bitwise(B, fa, fw):
+    # unit scales and g = 1, K = 1024: every partial sum is a multiple of 2^-2
+    # below 2^14, exact in FP32 in any order, so the row equals the oracle's
+    N, K = 200, 1024
+    g = datagen.rng(17)
+    grid = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    a = g.choice(grid, (1, K)).astype(np.float32)
+    w = g.choice(grid, (N, K)).astype(np.float32)
+    a[:, ::16] = 6.0
+    w[:, ::16] = -6.0
+    sp = SPECIAL if fw == "razer_w" else None
+    ca, sa, ga = O.quantize(a, fa, 16, O.ABSMAX, O.G_NONE)
+    cw, sw, gw = O.quantize(w, fw, 16, O.ABSMAX, O.G_NONE, special=sp)
+    ref = O.gemm_rows(fa, ca, sa, ga, fw, cw, sw, gw, sp, 1, N, K)
+    case(f"gemm single row exact {fa}x{fw}")
+    got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp)
+    assert np.array_equal(got, ref)
