@@ -1949,7 +1949,10 @@ __device__ __forceinline__ void gemv_row(const GemmParams& p, int64_t n, int lan
 template <int FA, int FW, int JB>
 __global__ __launch_bounds__(256) void gemv_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform by construction; read through a scalar so that the compiler
+  // knows it, and the row's buffer views stay in scalar registers (a view it
+  // takes for per-lane data is applied by a loop over the distinct values)
+  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const uint32_t sp_lo = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[0], (_Float16)p.w_special[1]});
   const uint32_t sp_hi = __builtin_bit_cast(uint32_t, (half2v){(_Float16)p.w_special[2], (_Float16)p.w_special[3]});
