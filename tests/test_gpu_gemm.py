@@ -405,3 +405,32 @@ def test_gemm_single_row_exact_regime_bitwise(B, fa, fw):
     case(f"gemm single row exact {fa}x{fw}")
     got = gpu_gemm(B, fa, ca, sa, ga, fw, cw, sw, gw, sp)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("special", [(7.5, -3.5, 4.5, -6.5), (-7.5, 7.5, 3.5, -2.5)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_single_row_wide_specials(B, special, out_dtype):
+    # RaZeR-W tables with four-significant-bit specials (7.5, 6.5, 4.5): their
+    # f16 patterns need the low byte; the row sums stay exact
+    N, K = 700, 5120
+    a = datagen.student_t((1, K), 950, 4.0)
+    w = datagen.normal((N, K), 951, 0.02)
+    ca, sa, ga = oquant(a, "razer_a")
+    cw, sw, gw = oquant(w, "razer_w", special=special)
+    ref = O.gemm_rows("razer_a", ca, sa, ga, "razer_w", cw, sw, gw, special, 1, N, K)
+    case(f"gemm single row wide specials {special} {out_dtype}")
+    got = gpu_gemm(B, "razer_a", ca, sa, ga, "razer_w", cw, sw, gw, special, out_dtype)
+    check(got, ref, out_dtype)
+    # the same weight in the exact regime: unit scales, g = 1, K = 1024
+    M1, K1 = 1, 1024
+    g = datagen.rng(952)
+    grid = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    a1 = g.choice(grid, (M1, K1)).astype(np.float32)
+    w1 = np.concatenate([g.choice(grid, (64, K1)), g.choice(np.array(special, np.float32), (64, K1))]).astype(np.float32)
+    a1[:, ::16] = 6.0
+    w1[:, ::16] = -6.0
+    ca1, sa1, ga1 = O.quantize(a1, "nvfp4", 16, O.ABSMAX, O.G_NONE)
+    cw1, sw1, gw1 = O.quantize(w1, "razer_w", 16, O.ABSMAX, O.G_NONE, special=special)
+    ref1 = O.gemm_rows("nvfp4", ca1, sa1, ga1, "razer_w", cw1, sw1, gw1, special, M1, 128, K1)
+    got1 = gpu_gemm(B, "nvfp4", ca1, sa1, ga1, "razer_w", cw1, sw1, gw1, special)
+    assert np.array_equal(got1, ref1)
