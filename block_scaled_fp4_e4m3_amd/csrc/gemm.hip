@@ -1486,10 +1486,11 @@ __device__ __forceinline__ void sm_decode(const uint4& c, uint32_t sc, uint32_t 
 // at those codes gives u, and fma(u, special * scale, value * scale) is
 // special * scale there (value * scale = -0) and value * scale elsewhere.
 // sc: the lane's two scale bytes (blocks of words 0-1 and 2-3).
-__device__ __forceinline__ float e3m3_f32(uint32_t k) {
-  const uint32_t e = k >> 3, m = k & 7u;
-  return e == 0 ? (float)m * 0x1p-5f : __uint_as_float(((e + 124u) << 23) | (m << 20));
-}
+// E3M3 code k (0..63) as FP32: the E4M3 code with the same bits has the
+// value 2^-4 times as large (bias 7 against 3, subnormals alike), so the
+// hardware FP8 decode with the exact power-of-two scale 16 gives it in one
+// instruction
+__device__ __forceinline__ float e3m3_f32(uint32_t k) { return __builtin_amdgcn_cvt_scalef32_f32_fp8(k, 16.0f, 0); }
 
 template <int F>
 __device__ __forceinline__ void sm_decode_bf16(const uint4& c, uint32_t sc, const float* special, uint4 (&out)[4]) {
